@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""GQLA decode attention benchmark on one MI355X.
+
+Workload: the flagship decode step, bf16, batch 128, h_q = 128 query heads in
+g = 8 groups (16 heads per group), latent width r_kv = 512, rotary key width
+d_R = 64, per-group head width d_h = 128, uniform context 8192, s_q = 1.
+Synthetic seeded inputs (synth.inputs), resident in HBM before timing.
+
+A step is one pass of the whole hot path over the batch: the MQA-absorb path
+(query absorption, latent attention with split-K, log-sum-exp combine with
+the fused W_UV up-projection) and the GQA path (attention over the expanded
+group rows with split-K, combine).  The group rows are expanded once per
+sequence beforehand (the method expands the latent once, not per step); that
+expansion is timed on its own and reported as expand_ms.
+
+Prints ONE JSON line: query-tokens/s of the step (batch * s_q / step time),
+per-path times and roofline fractions, the roofline object of the dominant
+kernel (HIP events around that kernel on its own stream) and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode query-tokens/s + % HBM/MFMA roofline, h_q=128 g=8 ctx 8K, both paths"
+PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
+COPY_BYTES = 1 << 30       # plain device copy run once per bench (counter calibration)
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (CPU baseline and its sampled agreement check)")
+    return ap.parse_args(argv)
+
+
+def sources_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, digest):
+    """Counter-derived HBM bytes per launch from profiles/traffic.json, if taken on this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, budget_s, gpu_out):
+    """fp64 oracle (absorb and GQA forms, expansion untimed) on sampled sequences.
+
+    gpu_out maps path -> device output [B][s_q][h_q][d_h]; the oracle results of the
+    sampled sequences are also compared with it (|gpu - oracle| / (2e-3 + 2e-2 |oracle|)).
+    """
+    import numpy as np
+    import oracle
+    import synth
+    from synth.inputs import sample_sequences
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    qn, qr = synth.queries(cfg)
+    w_uk, w_uv = synth.up_weights(cfg)
+    spent, n, worst = 0.0, 0, 0.0
+    for b in sample_sequences(cfg, 8):
+        L = synth.ctx_len(cfg, b)
+        rows = synth.latent_rows(cfg, b, L)
+        t0 = time.perf_counter()
+        oa, _ = oracle.absorb_decode(rows, qn[b], qr[b], w_uk, w_uv, L, cfg.scale)
+        t1 = time.perf_counter()
+        gr = oracle.expand_groups(rows, w_uk, w_uv)
+        t2 = time.perf_counter()
+        og, _ = oracle.gqa_decode(gr, qn[b], qr[b], cfg.g, L, cfg.scale)
+        t3 = time.perf_counter()
+        spent += (t1 - t0) + (t3 - t2)
+        n += 1
+        for path, ref in (("absorb", oa), ("gqa", og)):
+            got = gpu_out[path][b].float().cpu().numpy().astype(np.float64)
+            worst = max(worst, float(np.max(np.abs(got - ref) / (2e-3 + 2e-2 * np.abs(ref)))))
+        if spent >= budget_s:
+            break
+    rec = {"value": round(n * cfg.s_q / spent, 3), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"{n} of {cfg.batch} sequences at ctx {cfg.ctx[0]}: fp64 numpy oracle, absorb form + "
+                     f"GQA form per sequence (expansion untimed), {spent:.1f} s"}
+    parity = {"sequences": n, "max_err_over_tol": round(worst, 4), "ok": worst <= 1.0}
+    return rec, parity
+
+
+def main(argv=None):
+    args = parse(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the decode path runs on a single MI355X.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from latent_kv_cache_amd import gqla
+    from latent_kv_cache_amd import roofline as rf
+    from synth.device import make_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gqla.load()
+    cfg = synth.config(3)
+    t_gen = time.perf_counter()
+    w = make_workload(cfg, device=dev)
+    t_gen = time.perf_counter() - t_gen
+    B, S = cfg.batch, w.max_ctx
+    total_ctx = int(w.lens.sum())
+    sh = gqla.make_shape(cfg.h_q, cfg.g, cfg.r_kv, cfg.d_r, cfg.d_h, cfg.s_q, cfg.scale, gqla.BF16)
+
+    # plain copy of known size: reference point for the HBM byte counters of profiled runs
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    del src, dst
+
+    width = 2 * cfg.g * cfg.d_h + cfg.d_r
+    gc = torch.empty((B, S, width), dtype=torch.bfloat16, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gqla.expand_groups(sh, w.latent, w.w_uk, w.w_uv, w.ctx_lens, gc)
+    e1.record()
+    torch.cuda.synchronize()
+    expand_ms = e0.elapsed_time(e1)
+
+    out_a = torch.empty((B, cfg.s_q, cfg.h_q, cfg.d_h), dtype=torch.bfloat16, device=dev)
+    out_g = torch.empty_like(out_a)
+    ws_a = gqla.alloc_workspace(sh, gqla.ABSORB, B, S, 0, dev)
+    ws_g = gqla.alloc_workspace(sh, gqla.GQA, B, S, 0, dev)
+    split_a = gqla.plan_splits(sh, gqla.ABSORB, B, S, 0)
+    split_g = gqla.plan_splits(sh, gqla.GQA, B, S, 0)
+
+    def absorb():
+        gqla.decode_absorb(sh, w.q_nope, w.q_rope, w.w_uk, w.w_uv, w.latent, w.ctx_lens, out_a, None, ws_a)
+
+    def gqa():
+        gqla.decode_gqa(sh, w.q_nope, w.q_rope, gc, w.ctx_lens, out_g, None, ws_g)
+
+    for _ in range(args.warmup):
+        absorb()
+        gqa()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = {k: [mk() for _ in range(K)] for k in ("a0", "a1", "ak0", "ak1", "g0", "g1", "gk0", "gk1")}
+    for lst in ev.values():        # materialise the events before the library records them
+        for e in lst:
+            e.record()
+    torch.cuda.synchronize()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev["a0"][i].record()
+        gqla.set_kernel_events(ev["ak0"][i], ev["ak1"][i])
+        absorb()
+        ev["a1"][i].record()
+        ev["g0"][i].record()
+        gqla.set_kernel_events(ev["gk0"][i], ev["gk1"][i])
+        gqa()
+        ev["g1"][i].record()
+    gqla.set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    def avg(a, b):
+        return float(np.mean([ev[a][i].elapsed_time(ev[b][i]) for i in range(K)]))
+
+    call_a, call_g = avg("a0", "a1"), avg("g0", "g1")
+    kern_a, kern_g = avg("ak0", "ak1"), avg("gk0", "gk1")
+
+    work_a = rf.step_work("absorb", cfg.h_q, cfg.g, cfg.s_q, total_ctx, B, cfg.r_kv, cfg.d_r, cfg.d_h)
+    work_g = rf.step_work("gqa", cfg.h_q, cfg.g, cfg.s_q, total_ctx, B, cfg.r_kv, cfg.d_r, cfg.d_h)
+    q_tokens = B * cfg.s_q
+
+    def path_rec(work, call_ms, kern_ms, splits, kernel):
+        t = call_ms * 1e-3
+        hbm = work.bytes / t / PEAK_HBM
+        mfma = work.flops / t / PEAK_BF16
+        roof_t = max(work.bytes / PEAK_HBM, work.flops / PEAK_BF16)
+        return {"ms": round(call_ms, 4), "tokens_per_s": round(q_tokens / t, 1),
+                "hbm_frac": round(hbm, 4), "mfma_frac": round(mfma, 4),
+                "roofline_frac": round(roof_t / t, 4),
+                "roofline_tokens_per_s": round(q_tokens / roof_t, 1),
+                "alg_bytes": work.bytes, "alg_flops": work.flops,
+                "main_kernel": kernel, "main_kernel_ms": round(kern_ms, 4),
+                "n_split": splits[0], "chunk": splits[1]}
+
+    paths = {"absorb": path_rec(work_a, call_a, kern_a, split_a, "absorb_decode_kernel<8>"),
+             "gqa": path_rec(work_g, call_g, kern_g, split_g, "gqa_decode_kernel<8, 8>")}
+
+    # dominant kernel: the longer of the two main attention kernels
+    kernel_src = ["latent_kv_cache_amd/csrc/decode_bf16.hip", "latent_kv_cache_amd/csrc/common.h"]
+    digest = sources_digest(kernel_src)
+    if kern_g >= kern_a:
+        # bytes per launch: expanded rows of every cached token, queries in, outputs out
+        alg = (rf.gqa_bytes_per_token(cfg.g, cfg.d_h, cfg.d_r) * total_ctx
+               + q_tokens * cfg.h_q * (cfg.d_h + cfg.d_r + cfg.d_h) * 2)
+        achieved = alg / (kern_g * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("gqa_decode", digest),
+                "kernel": "gqa_decode_kernel<8, 8>", "alg_bytes_per_launch": alg, "avg_ms": round(kern_g, 4)}
+    else:
+        alg = (rf.absorb_bytes_per_token(cfg.r_kv, cfg.d_r) * total_ctx
+               + q_tokens * cfg.h_q * (cfg.r_kv + cfg.d_r + cfg.d_h) * 2 + cfg.g * cfg.d_h * cfg.r_kv * 2)
+        achieved = alg / (kern_a * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("absorb_decode", digest),
+                "kernel": "absorb_decode_kernel<8>", "alg_bytes_per_launch": alg, "avg_ms": round(kern_a, 4)}
+
+    cpu, parity = (None, None) if args.no_cpu_baseline else cpu_baseline(
+        cfg, args.cpu_seconds, {"absorb": out_a, "gqa": out_g})
+
+    rec = {
+        "metric": METRIC,
+        "value": round(q_tokens / (ms_per_step * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gqla-decode-flagship: both paths, bf16, batch 128, h_q 128, g 8, r_kv 512, "
+                               "d_R 64, d_h 128, ctx 8192 uniform, s_q 1",
+                   "batch": B, "ctx": int(cfg.ctx[0]), "h_q": cfg.h_q, "g": cfg.g, "s_q": cfg.s_q,
+                   "paths": ["absorb", "gqa"]},
+        "paths": paths,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "expand_ms": round(expand_ms, 3),
+        "parity": parity,
+        "input_gen_s": round(t_gen, 1),
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

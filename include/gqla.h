@@ -1,0 +1,147 @@
+/*
+ * gqla.h - C ABI of libgqla, MI355X (gfx950) GQLA decode attention.
+ *
+ * Method: "GQLA: Group-Query Latent Attention for Hardware-Adaptive LLM
+ * Decoding" (gist.science explainer page), technical summary section 2
+ * (Methodology: Architecture, Path selection) and section 1 (Problem).
+ *
+ * GQLA keeps, per cached token t, one latent row c_t (width r_kv) and one
+ * shared rotary key k_R,t (width d_r), and g group-indexed up-projections
+ * W_UK[j], W_UV[j] (each d_h x r_kv).  Query head i (of h_q) belongs to group
+ * j(i) = i / (h_q / g).  Its key for token t is [W_UK[j] c_t | k_R,t] and its
+ * value W_UV[j] c_t.  Two algebraically equal decode paths read this:
+ *   - MQA-absorb (section 2, memory-friendly path): W_UK is folded into the
+ *     query and W_UV applied after attention; every head attends to the
+ *     shared latent rows [c_t | k_R,t] (gqla_decode_absorb);
+ *   - GQA (section 2, compute-friendly path): the latent is expanded once into
+ *     g groups of K/V (gqla_expand_groups), and decode runs ordinary grouped
+ *     attention over the expanded rows (gqla_decode_gqa).
+ * Each step reads the whole cached history (section 1).  With s_q query
+ * tokens per step (multi-token prediction, section 2 Path selection) the s_q
+ * new tokens are the last s_q cached rows of the sequence and query s sees
+ * rows t <= L_b - s_q + s.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, in the
+ *     dtype of shape->dtype (bf16 or fp32; one dtype per call), row-major.
+ *     ctx_lens is a device int32[batch].  The library allocates nothing and
+ *     keeps no state besides a per-device cache of the compute-unit count.
+ *   - q_rope and the k_R columns of the cache hold keys/queries with the
+ *     rotary embedding already applied.
+ *   - stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work on it and never synchronise; results are ready when the stream is.
+ *   - Arguments are validated on the host before any launch; a failed check
+ *     returns a non-zero status and enqueues nothing.  gqla_last_error()
+ *     then names the offending argument.  Launch failures map to GQLA_ERR_HIP.
+ *   - ctx_lens contents are not read on the host.  Kernels clamp L_b to
+ *     [0, max_ctx]; a query that sees no row returns o = 0, lse = -inf.
+ *   - Thread safety: calls are reentrant; concurrent calls must use distinct
+ *     workspaces.
+ */
+#ifndef GQLA_H
+#define GQLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqla_status {
+    GQLA_OK = 0,
+    GQLA_ERR_INVALID_ARG = 1,   /* null pointer, bad size/stride/alignment, h_q % g != 0, ... */
+    GQLA_ERR_UNSUPPORTED = 2,   /* valid but not built: dims or group layout without a kernel */
+    GQLA_ERR_WORKSPACE = 3,     /* workspace null or smaller than gqla_workspace_size() */
+    GQLA_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} gqla_status;
+
+typedef enum gqla_dtype { GQLA_BF16 = 0, GQLA_F32 = 1 } gqla_dtype;
+typedef enum gqla_path { GQLA_PATH_ABSORB = 0, GQLA_PATH_GQA = 1 } gqla_path;
+
+/* Model and step shape (section 2, Architecture): h_q query heads, g groups,
+ * latent width r_kv, rotary key width d_r, per-group head width d_h, s_q query
+ * tokens per step (1..4), softmax scale applied to q.k, storage dtype.
+ * Kernels built: bf16 with r_kv=512, d_r=64, d_h=128 (MFMA path); fp32 with
+ * r_kv <= 1024, d_r <= 256, d_h <= 256 (vector path). */
+typedef struct gqla_shape {
+    int32_t h_q, g, r_kv, d_r, d_h, s_q;
+    float scale;
+    int32_t dtype;              /* gqla_dtype */
+} gqla_shape;
+
+/* Bytes of device workspace a decode call needs (split-K partials, and for the
+ * absorb path the absorbed queries).  num_splits: 0 = automatic, else an upper
+ * bound on context chunks per sequence.  Returns GQLA_OK and writes *bytes. */
+gqla_status gqla_workspace_size(const gqla_shape* shape, int32_t path, int32_t batch,
+                                int32_t max_ctx, int32_t num_splits, size_t* bytes);
+
+/* Number of context chunks per sequence and chunk length (tokens) that a decode
+ * call with these arguments uses.  Host-only; for planning and tests. */
+gqla_status gqla_plan_splits(const gqla_shape* shape, int32_t path, int32_t batch,
+                             int32_t max_ctx, int32_t num_splits,
+                             int32_t* n_split, int32_t* chunk);
+
+/* Expand latent rows once into g groups of K and V (section 2, GQA path: the
+ * latent is expanded into g K/V groups so decode need not re-expand it each step).
+ *   latent      [batch][latent_bstride] elements; sequence b's row t starts at
+ *               latent + b*latent_bstride + t*(r_kv+d_r) and is [c_t | k_R,t].
+ *   w_uk, w_uv  [g][d_h][r_kv].
+ *   group_cache [batch][group_bstride]; row t of sequence b (width 2 g d_h + d_r)
+ *               is written as [W_UK[0]c_t .. W_UK[g-1]c_t | W_UV[0]c_t .. W_UV[g-1]c_t | k_R,t],
+ *               for row_begin <= t < L_b only (other rows are not touched).
+ *   Products accumulate in fp32 and are rounded once (RNE) to the dtype.
+ *   Strides are in elements, multiples of 8, and at least max_ctx * row width. */
+gqla_status gqla_expand_groups(const gqla_shape* shape, int32_t batch, int32_t max_ctx,
+                               const void* latent, int64_t latent_bstride,
+                               const void* w_uk, const void* w_uv,
+                               const int32_t* ctx_lens, int32_t row_begin,
+                               void* group_cache, int64_t group_bstride, void* stream);
+
+/* MQA-absorb decode (section 2, memory-friendly path, "identical to MLA"):
+ * q~ = W_UK[j]^T q_nope per head, scores s_t = scale [q~ | q_rope].[c_t | k_R,t],
+ * u = softmax-weighted sum of c_t, o = W_UV[j] u.
+ *   q_nope [batch][s_q][h_q][d_h], q_rope [batch][s_q][h_q][d_r]
+ *   w_uk, w_uv [g][d_h][r_kv]; latent as in gqla_expand_groups
+ *   out [batch][s_q][h_q][d_h] (dtype); lse (nullable) fp32 [batch][s_q][h_q],
+ *   natural-log log-sum-exp of the scaled scores.
+ * Context is split into chunks (split-K); per-chunk partials in the workspace
+ * are merged by their log-sum-exp. */
+gqla_status gqla_decode_absorb(const gqla_shape* shape, int32_t batch, int32_t max_ctx,
+                               const void* q_nope, const void* q_rope,
+                               const void* w_uk, const void* w_uv,
+                               const void* latent, int64_t latent_bstride,
+                               const int32_t* ctx_lens, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t num_splits, void* stream);
+
+/* GQA decode over expanded rows (section 2, compute-friendly path): head i of
+ * group j scores [q_nope | q_rope].[K_j,t | k_R,t] and averages V_j,t.
+ *   group_cache as written by gqla_expand_groups; other arguments as in
+ *   gqla_decode_absorb. */
+gqla_status gqla_decode_gqa(const gqla_shape* shape, int32_t batch, int32_t max_ctx,
+                            const void* q_nope, const void* q_rope,
+                            const void* group_cache, int64_t group_bstride,
+                            const int32_t* ctx_lens, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            int32_t num_splits, void* stream);
+
+/* Timing hook for measurement tools.  When both are non-NULL, every later decode
+ * call on this thread records `before` (a hipEvent_t) on its stream right before
+ * launching its main attention kernel and `after` right after it, so that
+ * hipEventElapsedTime(before, after) is that kernel's duration.  The absorb
+ * prologue and the split-K combine fall outside the pair.  NULL, NULL turns it
+ * off.  The events are the caller's; the library only records them. */
+gqla_status gqla_set_kernel_events(void* before, void* after);
+
+/* Static description of a status code. */
+const char* gqla_status_string(gqla_status status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* gqla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQLA_H */

@@ -1,0 +1,325 @@
+// C-ABI host layer of libgqla: argument validation, split-K planning, workspace
+// layout and kernel launches on the caller's stream.  Declarations and the
+// contract of each entry point are in include/gqla.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/gqla.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+
+gqla_status fail(gqla_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+gqla_status ok() {
+    g_err[0] = '\0';
+    return GQLA_OK;
+}
+
+// Compute units of the current device, cached per device id.
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool is_bf16_mfma_shape(const gqla_shape& s) { return s.r_kv == 512 && s.d_r == 64 && s.d_h == 128; }
+
+gqla_status check_shape(const gqla_shape* sp, int path) {
+    if (!sp) return fail(GQLA_ERR_INVALID_ARG, "shape is null");
+    const gqla_shape& s = *sp;
+    if (path != GQLA_PATH_ABSORB && path != GQLA_PATH_GQA) return fail(GQLA_ERR_INVALID_ARG, "path %d is neither absorb (0) nor gqa (1)", path);
+    if (s.h_q <= 0 || s.g <= 0 || s.r_kv <= 0 || s.d_r <= 0 || s.d_h <= 0)
+        return fail(GQLA_ERR_INVALID_ARG, "dims must be positive (h_q=%d g=%d r_kv=%d d_r=%d d_h=%d)", s.h_q, s.g, s.r_kv, s.d_r, s.d_h);
+    if (s.h_q % s.g != 0) return fail(GQLA_ERR_INVALID_ARG, "h_q=%d is not a multiple of g=%d", s.h_q, s.g);
+    if (s.s_q < 1 || s.s_q > 4) return fail(GQLA_ERR_INVALID_ARG, "s_q=%d outside 1..4", s.s_q);
+    if (!(s.scale > 0.f) || !std::isfinite(s.scale)) return fail(GQLA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (s.r_kv % 8 || s.d_r % 8 || s.d_h % 8) return fail(GQLA_ERR_INVALID_ARG, "r_kv, d_r and d_h must be multiples of 8");
+    if (s.dtype == GQLA_BF16) {
+        if (!is_bf16_mfma_shape(s))
+            return fail(GQLA_ERR_UNSUPPORTED, "bf16 kernels are built for r_kv=512, d_r=64, d_h=128 (got %d, %d, %d)", s.r_kv, s.d_r, s.d_h);
+        if (path == GQLA_PATH_ABSORB && s.h_q % 16 != 0)
+            return fail(GQLA_ERR_UNSUPPORTED, "bf16 absorb path needs h_q %% 16 == 0 (got %d)", s.h_q);
+        if (path == GQLA_PATH_GQA && !gqla::gqa_bf16_supported(s.g, s.s_q * (s.h_q / s.g)))
+            return fail(GQLA_ERR_UNSUPPORTED, "bf16 GQA path is built for g in {1,2,4,8} (got %d)", s.g);
+    } else if (s.dtype == GQLA_F32) {
+        if (s.r_kv > 1024 || s.d_r > 256 || s.d_h > 256)
+            return fail(GQLA_ERR_UNSUPPORTED, "fp32 kernels need r_kv <= 1024, d_r <= 256, d_h <= 256");
+    } else {
+        return fail(GQLA_ERR_INVALID_ARG, "unknown dtype %d", s.dtype);
+    }
+    return GQLA_OK;
+}
+
+struct Plan {
+    int n_split, chunk;
+};
+
+// Context chunking.  Chunks are multiples of the bf16 token tile; the fp32 path keeps
+// a chunk's scores in LDS, so its chunks are capped.  Automatic mode aims for at
+// least one workgroup per compute unit and chunks of at most 4096 tokens (so ragged
+// batches spread over the CUs); an explicit num_splits is an upper bound on chunks.
+Plan plan(const gqla_shape& s, int path, int batch, int max_ctx, int num_splits) {
+    const int align = s.dtype == GQLA_BF16 ? gqla::kBf16TokenTile : 1;
+    const int ctx = max_ctx > 0 ? max_ctx : 1;
+    int want;
+    if (num_splits > 0) {
+        want = num_splits;
+    } else {
+        int units = batch > 0 ? batch : 1;
+        if (s.dtype == GQLA_BF16 && path == GQLA_PATH_ABSORB)
+            units *= (s.s_q * s.h_q + gqla::kAbsorbRowsPerBlock - 1) / gqla::kAbsorbRowsPerBlock;
+        const int cus = device_cus();
+        want = (cus + units - 1) / units;
+        const int by_len = (ctx + 4095) / 4096;
+        if (by_len > want) want = by_len;
+    }
+    if (want > ctx) want = ctx;
+    if (want < 1) want = 1;
+    int chunk = (ctx + want - 1) / want;
+    chunk = (chunk + align - 1) / align * align;
+    if (s.dtype == GQLA_F32 && chunk > gqla::kF32MaxChunk) chunk = gqla::kF32MaxChunk;
+    Plan p;
+    p.chunk = chunk;
+    p.n_split = (ctx + chunk - 1) / chunk;
+    return p;
+}
+
+struct Layout {
+    size_t part_o, part_lse, qhat, total;
+};
+
+Layout layout(const gqla_shape& s, int path, int batch, const Plan& p) {
+    const size_t rows = (size_t)batch * s.s_q * s.h_q;
+    Layout l;
+    l.part_o = 0;
+    l.part_lse = align256(l.part_o + (size_t)p.n_split * rows * s.d_h * sizeof(float));
+    l.qhat = align256(l.part_lse + (size_t)p.n_split * rows * sizeof(float));
+    size_t end = l.qhat;
+    if (path == GQLA_PATH_ABSORB && s.dtype == GQLA_BF16) end = align256(l.qhat + rows * (s.r_kv + s.d_r) * 2);
+    l.total = end;
+    return l;
+}
+
+gqla_status check_sizes(int batch, int max_ctx) {
+    if (batch < 0) return fail(GQLA_ERR_INVALID_ARG, "batch=%d < 0", batch);
+    if (max_ctx < 0) return fail(GQLA_ERR_INVALID_ARG, "max_ctx=%d < 0", max_ctx);
+    return GQLA_OK;
+}
+
+gqla_status check_ptr(const void* p, const char* name) {
+    if (!p) return fail(GQLA_ERR_INVALID_ARG, "%s is null", name);
+    if (!aligned16(p)) return fail(GQLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return GQLA_OK;
+}
+
+gqla_status check_stride(int64_t stride, int64_t row_width, int max_ctx, const char* name) {
+    if (stride % 8 != 0) return fail(GQLA_ERR_INVALID_ARG, "%s=%lld is not a multiple of 8 elements", name, (long long)stride);
+    if (stride < row_width * (int64_t)max_ctx)
+        return fail(GQLA_ERR_INVALID_ARG, "%s=%lld < max_ctx * row width = %lld", name, (long long)stride,
+                    (long long)(row_width * (int64_t)max_ctx));
+    return GQLA_OK;
+}
+
+#define TRY(x)                               \
+    do {                                     \
+        gqla_status _st = (x);               \
+        if (_st != GQLA_OK) return _st;      \
+    } while (0)
+
+gqla_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(GQLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+gqla_status decode_common(int path, const gqla_shape* sp, int32_t batch, int32_t max_ctx, const void* q_nope,
+                          const void* q_rope, const void* w_uk, const void* w_uv, const void* cache,
+                          int64_t bstride, const int32_t* ctx_lens, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, int32_t num_splits, void* stream) {
+    TRY(check_shape(sp, path));
+    TRY(check_sizes(batch, max_ctx));
+    if (num_splits < 0) return fail(GQLA_ERR_INVALID_ARG, "num_splits=%d < 0", num_splits);
+    const gqla_shape& s = *sp;
+    if (batch == 0) return ok();
+    const int64_t width = path == GQLA_PATH_ABSORB ? s.r_kv + s.d_r : 2LL * s.g * s.d_h + s.d_r;
+    TRY(check_ptr(q_nope, "q_nope"));
+    TRY(check_ptr(q_rope, "q_rope"));
+    if (path == GQLA_PATH_ABSORB) {
+        TRY(check_ptr(w_uk, "w_uk"));
+        TRY(check_ptr(w_uv, "w_uv"));
+    }
+    TRY(check_ptr(cache, path == GQLA_PATH_ABSORB ? "latent" : "group_cache"));
+    TRY(check_stride(bstride, width, max_ctx, path == GQLA_PATH_ABSORB ? "latent_bstride" : "group_bstride"));
+    if (!ctx_lens) return fail(GQLA_ERR_INVALID_ARG, "ctx_lens is null");
+    TRY(check_ptr(out, "out"));
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(GQLA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+    const Plan p = plan(s, path, batch, max_ctx, num_splits);
+    const Layout lay = layout(s, path, batch, p);
+    if (!workspace) return fail(GQLA_ERR_WORKSPACE, "workspace is null (%zu bytes needed)", lay.total);
+    if (!aligned16(workspace)) return fail(GQLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < lay.total)
+        return fail(GQLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, lay.total);
+
+    gqla::DecodeArgs a;
+    a.h_q = s.h_q;
+    a.g = s.g;
+    a.r_kv = s.r_kv;
+    a.d_r = s.d_r;
+    a.d_h = s.d_h;
+    a.s_q = s.s_q;
+    a.scale = s.scale;
+    a.batch = batch;
+    a.max_ctx = max_ctx;
+    a.n_split = p.n_split;
+    a.chunk = p.chunk;
+    a.q_nope = q_nope;
+    a.q_rope = q_rope;
+    a.w_uk = w_uk;
+    a.w_uv = w_uv;
+    a.cache = cache;
+    a.bstride = bstride;
+    a.ctx_lens = ctx_lens;
+    a.out = out;
+    a.lse = lse;
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+    a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
+    a.qhat = ws + lay.qhat;
+    a.ev_before = g_ev_before;
+    a.ev_after = g_ev_after;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (s.dtype == GQLA_BF16) {
+        e = path == GQLA_PATH_ABSORB ? gqla::launch_absorb_bf16(a, st) : gqla::launch_gqa_bf16(a, st);
+    } else {
+        e = path == GQLA_PATH_ABSORB ? gqla::launch_absorb_f32(a, st) : gqla::launch_gqa_f32(a, st);
+    }
+    if (e != hipSuccess) return hip_status(e, "decode launch");
+    return hip_status(gqla::launch_combine(a, s.dtype == GQLA_BF16, st), "combine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+gqla_status gqla_workspace_size(const gqla_shape* shape, int32_t path, int32_t batch, int32_t max_ctx,
+                                int32_t num_splits, size_t* bytes) {
+    TRY(check_shape(shape, path));
+    TRY(check_sizes(batch, max_ctx));
+    if (num_splits < 0) return fail(GQLA_ERR_INVALID_ARG, "num_splits=%d < 0", num_splits);
+    if (!bytes) return fail(GQLA_ERR_INVALID_ARG, "bytes is null");
+    const Plan p = plan(*shape, path, batch, max_ctx, num_splits);
+    *bytes = layout(*shape, path, batch, p).total;
+    return ok();
+}
+
+gqla_status gqla_plan_splits(const gqla_shape* shape, int32_t path, int32_t batch, int32_t max_ctx,
+                             int32_t num_splits, int32_t* n_split, int32_t* chunk) {
+    TRY(check_shape(shape, path));
+    TRY(check_sizes(batch, max_ctx));
+    if (num_splits < 0) return fail(GQLA_ERR_INVALID_ARG, "num_splits=%d < 0", num_splits);
+    if (!n_split || !chunk) return fail(GQLA_ERR_INVALID_ARG, "n_split or chunk is null");
+    const Plan p = plan(*shape, path, batch, max_ctx, num_splits);
+    *n_split = p.n_split;
+    *chunk = p.chunk;
+    return ok();
+}
+
+gqla_status gqla_expand_groups(const gqla_shape* shape, int32_t batch, int32_t max_ctx, const void* latent,
+                               int64_t latent_bstride, const void* w_uk, const void* w_uv, const int32_t* ctx_lens,
+                               int32_t row_begin, void* group_cache, int64_t group_bstride, void* stream) {
+    TRY(check_shape(shape, GQLA_PATH_GQA));
+    TRY(check_sizes(batch, max_ctx));
+    const gqla_shape& s = *shape;
+    if (row_begin < 0) return fail(GQLA_ERR_INVALID_ARG, "row_begin=%d < 0", row_begin);
+    if (batch == 0 || row_begin >= max_ctx) return ok();
+    TRY(check_ptr(latent, "latent"));
+    TRY(check_ptr(w_uk, "w_uk"));
+    TRY(check_ptr(w_uv, "w_uv"));
+    TRY(check_ptr(group_cache, "group_cache"));
+    if (!ctx_lens) return fail(GQLA_ERR_INVALID_ARG, "ctx_lens is null");
+    TRY(check_stride(latent_bstride, s.r_kv + s.d_r, max_ctx, "latent_bstride"));
+    TRY(check_stride(group_bstride, 2LL * s.g * s.d_h + s.d_r, max_ctx, "group_bstride"));
+    gqla::ExpandArgs a;
+    a.h_q = s.h_q;
+    a.g = s.g;
+    a.r_kv = s.r_kv;
+    a.d_r = s.d_r;
+    a.d_h = s.d_h;
+    a.batch = batch;
+    a.max_ctx = max_ctx;
+    a.row_begin = row_begin;
+    a.latent = latent;
+    a.latent_bstride = latent_bstride;
+    a.w_uk = w_uk;
+    a.w_uv = w_uv;
+    a.ctx_lens = ctx_lens;
+    a.group_cache = group_cache;
+    a.group_bstride = group_bstride;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = s.dtype == GQLA_BF16 ? gqla::launch_expand_bf16(a, st) : gqla::launch_expand_f32(a, st);
+    return hip_status(e, "expand launch");
+}
+
+gqla_status gqla_decode_absorb(const gqla_shape* shape, int32_t batch, int32_t max_ctx, const void* q_nope,
+                               const void* q_rope, const void* w_uk, const void* w_uv, const void* latent,
+                               int64_t latent_bstride, const int32_t* ctx_lens, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream) {
+    return decode_common(GQLA_PATH_ABSORB, shape, batch, max_ctx, q_nope, q_rope, w_uk, w_uv, latent,
+                         latent_bstride, ctx_lens, out, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+gqla_status gqla_decode_gqa(const gqla_shape* shape, int32_t batch, int32_t max_ctx, const void* q_nope,
+                            const void* q_rope, const void* group_cache, int64_t group_bstride,
+                            const int32_t* ctx_lens, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            int32_t num_splits, void* stream) {
+    return decode_common(GQLA_PATH_GQA, shape, batch, max_ctx, q_nope, q_rope, nullptr, nullptr, group_cache,
+                         group_bstride, ctx_lens, out, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+gqla_status gqla_set_kernel_events(void* before, void* after) {
+    if ((before == nullptr) != (after == nullptr))
+        return fail(GQLA_ERR_INVALID_ARG, "set both kernel events or neither");
+    g_ev_before = static_cast<hipEvent_t>(before);
+    g_ev_after = static_cast<hipEvent_t>(after);
+    return ok();
+}
+
+const char* gqla_status_string(gqla_status status) {
+    switch (status) {
+        case GQLA_OK: return "ok";
+        case GQLA_ERR_INVALID_ARG: return "invalid argument";
+        case GQLA_ERR_UNSUPPORTED: return "unsupported shape";
+        case GQLA_ERR_WORKSPACE: return "workspace missing or too small";
+        case GQLA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* gqla_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,508 @@
+// bf16 MFMA decode kernels for gfx950: GQA path and MQA-absorb path.
+//
+// Method: "GQLA: Group-Query Latent Attention for Hardware-Adaptive LLM
+// Decoding", technical summary section 2 (Architecture).  Both paths compute,
+// per sequence b, query token s and head i of group j = i / (h_q/g), softmax
+// attention over the visible cached tokens t <= L_b - s_q + s:
+//   GQA:    score_t = scale [q^N | q^R].[K_j,t | k_R,t],  o = sum_t p_t V_j,t
+//   absorb: score_t = scale [W_UK[j]^T q^N | q^R].[c_t | k_R,t],
+//           o = W_UV[j] sum_t p_t c_t
+// over one context chunk per workgroup (split-K).  Each workgroup writes the
+// chunk's normalised output and its log-sum-exp; launch_combine merges them.
+//
+// Tiling.  A workgroup streams its chunk in tiles of 32 cache rows.  A tile is
+// one contiguous span of HBM (rows of a sequence are packed), loaded with
+// 16-byte vector loads into registers one tile ahead and stored into LDS with
+// a 16-byte pad per row, which makes the MFMA operand reads bank-conflict free.
+// Each wave owns 16 query rows (the M = 16 side of the 16x16x32 MFMA: the 16
+// heads of a group on the GQA path at h_q/g = 16, or 16 of the heads sharing
+// the latent on the absorb path) and keeps its queries and accumulators in
+// registers:
+//   S^T[token][row] = K_tile . Q^T   (A = cache rows from LDS, B = queries)
+//   O^T[feat][row] += V_tile^T . P^T (A = cache columns from LDS, B = P)
+// so the softmax state of a row lives in the four lanes l%16 + 16q.
+#include "common.h"
+#include "launch.h"
+
+namespace gqla {
+
+namespace {
+
+constexpr int DH = 128;   // per-group key/value width
+constexpr int DR = 64;    // rotary key width
+constexpr int RK = 512;   // latent width
+constexpr int TT = 32;    // tokens per tile
+
+// Token held by k-slot e (0..7) of lane group q (0..3) in the P / V^T operands:
+// the softmax keeps S for tokens 16*(e/4) + 4q + (e%4), the D-layout of the two
+// 16-token halves of S^T.
+__device__ __forceinline__ int slot_token(int q, int e) { return 16 * (e >> 2) + 4 * q + (e & 3); }
+
+// Online-softmax update for one tile.  sc[e] are raw scores for slot_token(q4, e);
+// masked slots must hold -inf.  Returns P as the bf16 B operand and the factor
+// alpha by which the running accumulators must be rescaled.
+struct SoftmaxState {
+    float m;   // running max (log2 domain), identical in the 4 lanes of a row
+    float l;   // lane-partial running sum of exp2
+};
+
+__device__ __forceinline__ bf16x8 softmax_tile(SoftmaxState& st, float (&sc)[8], float& alpha) {
+    float mt = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
+    mt = wave_max16x4(mt);
+    const float mnew = fmaxf(st.m, mt);
+    const float muse = (mnew == kNegInf) ? 0.f : mnew;
+    alpha = fast_exp2(st.m - muse);
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(sc[e] - muse);
+        ps += p[e];
+    }
+    st.l = st.l * alpha + ps;
+    st.m = mnew;
+    u32x4 pk;
+    pk[0] = pack2f(p[0], p[1]);
+    pk[1] = pack2f(p[2], p[3]);
+    pk[2] = pack2f(p[4], p[5]);
+    pk[3] = pack2f(p[6], p[7]);
+    return as_bf16x8(pk);
+}
+
+// A operand of O^T += V^T P^T: lane (q4, r16) needs column `col` of the tile at the
+// eight slot tokens.
+__device__ __forceinline__ bf16x8 gather_col(const u16* lds, int stride, int q4, int col) {
+    u32x4 v;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const u16 lo = lds[slot_token(q4, 2 * h) * stride + col];
+        const u16 hi = lds[slot_token(q4, 2 * h + 1) * stride + col];
+        v[h] = pack2(lo, hi);
+    }
+    return as_bf16x8(v);
+}
+
+// Copy rows [row0, row0 + nrows) of a packed row-major span (width W elements) into
+// registers: chunk c = tid + k*NT of the tile, 16 bytes each.  Rows past nrows load zeros.
+template <int W, int NT, int NLOAD>
+__device__ __forceinline__ void load_tile(u32x4 (&reg)[NLOAD], const u16* __restrict__ base, int nrows, int tid) {
+    constexpr int CPR = W / 8;   // 16-byte chunks per row
+#pragma unroll
+    for (int k = 0; k < NLOAD; ++k) {
+        const int c = tid + k * NT;
+        const int r = c / CPR;
+        if (c < TT * CPR && r < nrows) {
+            reg[k] = *reinterpret_cast<const u32x4*>(base + (size_t)c * 8);
+        } else {
+            reg[k] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+template <int W, int STRIDE, int NT, int NLOAD>
+__device__ __forceinline__ void store_tile(u16* lds, const u32x4 (&reg)[NLOAD], int tid) {
+    constexpr int CPR = W / 8;
+#pragma unroll
+    for (int k = 0; k < NLOAD; ++k) {
+        const int c = tid + k * NT;
+        if (c < TT * CPR) {
+            const int r = c / CPR;
+            const int col = c - r * CPR;
+            *reinterpret_cast<u32x4*>(lds + r * STRIDE + col * 8) = reg[k];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// GQA decode.  grid = (n_split, batch, pair blocks); block = NW waves.  The
+// (group, 16-row tile) pairs of a sequence are numbered pair = j*RT + rt with
+// RT = ceil(rows_per_group / 16); block z handles pairs [z*NW, z*NW + NW).
+// Rows of group j are numbered rho = s*hpg + hh (query token s, head j*hpg + hh).
+// ---------------------------------------------------------------------------
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
+    const u16* __restrict__ q_nope, const u16* __restrict__ q_rope,
+    const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
+    int max_ctx, int h_q, int s_q, int chunk, int batch, float scale_log2,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    constexpr int W = 2 * G * DH + DR;
+    constexpr int STRIDE = W + 8;
+    constexpr int NT = NW * 64;
+    constexpr int NLOAD = (TT * (W / 8) + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) u16 lds[TT * STRIDE];
+
+    const int p = blockIdx.x, b = blockIdx.y;
+    const int L = clampi(ctx_lens[b], 0, max_ctx);
+    const int t0 = p * chunk;
+    if (t0 >= L) return;                      // uniform over the block
+    const int t1 = min(t0 + chunk, L);
+    const int ntiles = (t1 - t0 + TT - 1) / TT;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int q4 = lane >> 4, r16 = lane & 15;
+    const int hpg = h_q / G;
+    const int rows_g = s_q * hpg;
+    const int RT = (rows_g + 15) >> 4;
+    const int pair = blockIdx.z * NW + wave;
+    const bool active = pair < G * RT;
+    const int j = active ? pair / RT : 0;
+    const int rt = active ? pair - j * RT : 0;
+    const int rho = rt * 16 + r16;
+    const bool row_ok = active && rho < rows_g;
+    const int s = row_ok ? rho / hpg : 0;
+    const int h = j * hpg + (row_ok ? rho - s * hpg : 0);
+    const int nvis = clampi(L - s_q + s + 1, 0, L);
+    const int qrow = (b * s_q + s) * h_q + h;
+
+    // queries as the B operand of S^T = K Q^T: k-steps 0..3 over q^N, 4..5 over q^R
+    bf16x8 qv[6];
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) {
+        if (row_ok) {
+            qv[kk] = kk < 4 ? ld_bf16x8(q_nope + (size_t)qrow * DH + kk * 32 + q4 * 8)
+                            : ld_bf16x8(q_rope + (size_t)qrow * DR + (kk - 4) * 32 + q4 * 8);
+        } else {
+            qv[kk] = zero_bf16x8();
+        }
+    }
+
+    floatx4 oacc[DH / 16];
+#pragma unroll
+    for (int n = 0; n < DH / 16; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    SoftmaxState st{kNegInf, 0.f};
+
+    const u16* seq = cache + (size_t)b * bstride;
+    u32x4 reg[NLOAD];
+    load_tile<W, NT, NLOAD>(reg, seq + (size_t)t0 * W, min(TT, t1 - t0), tid);
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int tb = t0 + it * TT;
+        if (it > 0) __syncthreads();
+        store_tile<W, STRIDE, NT, NLOAD>(lds, reg, tid);
+        __syncthreads();
+        if (it + 1 < ntiles) {
+            const int tn = tb + TT;
+            load_tile<W, NT, NLOAD>(reg, seq + (size_t)tn * W, min(TT, t1 - tn), tid);
+        }
+        if (!active) continue;
+
+        float sc[8];
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            const u16* arow = lds + (th * 16 + r16) * STRIDE;
+#pragma unroll
+            for (int kk = 0; kk < 6; ++kk) {
+                const int col = kk < 4 ? j * DH + kk * 32 + q4 * 8 : 2 * G * DH + (kk - 4) * 32 + q4 * 8;
+                acc = mfma16(ld_bf16x8(arow + col), qv[kk], acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = tb + th * 16 + q4 * 4 + i;
+                sc[th * 4 + i] = (row_ok && t < t1 && t < nvis) ? acc[i] * scale_log2 : kNegInf;
+            }
+        }
+        float alpha;
+        const bf16x8 pb = softmax_tile(st, sc, alpha);
+        const int vcol = (G + j) * DH + r16;
+#pragma unroll
+        for (int n = 0; n < DH / 16; ++n) {
+            oacc[n] *= alpha;
+            oacc[n] = mfma16(gather_col(lds, STRIDE, q4, vcol + 16 * n), pb, oacc[n]);
+        }
+    }
+    if (!row_ok) return;
+
+    const float l = wave_sum16x4(st.l);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
+    float* po = part_o + prow * DH;
+#pragma unroll
+    for (int n = 0; n < DH / 16; ++n) {
+        *reinterpret_cast<floatx4*>(po + 16 * n + 4 * q4) = oacc[n] * inv;
+    }
+    if (q4 == 0) part_lse[prow] = l > 0.f ? (st.m + __log2f(l)) * kLn2 : kNegInf;
+}
+
+// ---------------------------------------------------------------------------
+// Absorb prologue: qhat[b][rho][0:512] = W_UK[j]^T q^N, qhat[b][rho][512:576] = q^R,
+// rho = s*h_q + h.  grid = (row blocks of 64, g); block = 4 waves.  The rows of
+// group j are numbered iota = (b*s_q + s)*hpg + hh.  W_UK[j] is staged in LDS
+// transposed ([r][d]) so the contraction over d reads 16 contiguous bytes.
+// ---------------------------------------------------------------------------
+constexpr int PRO_STRIDE = DH + 8;
+
+__global__ __launch_bounds__(256) void absorb_prologue_kernel(
+    const u16* __restrict__ q_nope, const u16* __restrict__ q_rope, const u16* __restrict__ w_uk,
+    u16* __restrict__ qhat, int batch, int h_q, int g, int s_q) {
+    __shared__ __attribute__((aligned(16))) u16 wt[RK * PRO_STRIDE];
+    const int j = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int q4 = lane >> 4, r16 = lane & 15;
+
+    const u16* wj = w_uk + (size_t)j * DH * RK;
+    // 128 x 512 -> transposed; chunk c: d = c % 128, r8 = c / 128 (consecutive lanes write
+    // consecutive d, i.e. consecutive LDS halfwords)
+    for (int c = tid; c < DH * (RK / 8); c += 256) {
+        const int d = c & (DH - 1);
+        const int r8 = c >> 7;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(wj + (size_t)d * RK + r8 * 8);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            wt[(r8 * 8 + 2 * h) * PRO_STRIDE + d] = (u16)(v[h] & 0xffffu);
+            wt[(r8 * 8 + 2 * h + 1) * PRO_STRIDE + d] = (u16)(v[h] >> 16);
+        }
+    }
+    __syncthreads();
+
+    const int hpg = h_q / g;
+    const int nrows = batch * s_q * hpg;
+    const int iota = blockIdx.x * 64 + wave * 16 + r16;
+    const bool ok = iota < nrows;
+    const int bs = ok ? iota / hpg : 0;
+    const int hh = ok ? iota - bs * hpg : 0;
+    const int b = bs / s_q, s = bs - (bs / s_q) * s_q;
+    const int h = j * hpg + hh;
+    const size_t qrow = ((size_t)b * s_q + s) * h_q + h;
+    const int RQ = s_q * h_q;
+    u16* dst = qhat + ((size_t)b * RQ + (size_t)s * h_q + h) * (RK + DR);
+
+    bf16x8 qb[DH / 32];
+#pragma unroll
+    for (int kd = 0; kd < DH / 32; ++kd) qb[kd] = ok ? ld_bf16x8(q_nope + qrow * DH + kd * 32 + q4 * 8) : zero_bf16x8();
+
+#pragma unroll 4
+    for (int mt = 0; mt < RK / 16; ++mt) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kd = 0; kd < DH / 32; ++kd) {
+            acc = mfma16(ld_bf16x8(wt + (mt * 16 + r16) * PRO_STRIDE + kd * 32 + q4 * 8), qb[kd], acc);
+        }
+        if (ok) {
+            u32x2 o;
+            o[0] = pack2f(acc[0], acc[1]);
+            o[1] = pack2f(acc[2], acc[3]);
+            *reinterpret_cast<u32x2*>(dst + mt * 16 + q4 * 4) = o;
+        }
+    }
+    if (ok) {
+        // q^R: 64 elements = 8 chunks of 16 bytes; lane group q4 copies chunks q4 and q4 + 4
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int off = (q4 + 4 * c) * 8;
+            *reinterpret_cast<u32x4*>(dst + RK + off) = *reinterpret_cast<const u32x4*>(q_rope + qrow * DR + off);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Absorb latent attention with fused W_UV.  grid = (n_split, batch, row blocks of
+// 128); block = NW waves; wave w owns query rows rho = z*128 + 16w + (0..15) of the
+// s_q*h_q rows (rho = s*h_q + h), all attending to the shared 576-wide rows.
+// After the chunk, u = P.C / l stays in registers and each group present in the
+// wave's rows applies W_UV[j] with MFMA, so the partial written is o_p (d_h wide).
+// ---------------------------------------------------------------------------
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
+    const u16* __restrict__ qhat, const u16* __restrict__ w_uv,
+    const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
+    int max_ctx, int h_q, int g, int s_q, int chunk, int batch, float scale_log2,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    constexpr int W = RK + DR;
+    constexpr int STRIDE = W + 8;
+    constexpr int NT = NW * 64;
+    constexpr int NLOAD = (TT * (W / 8) + NT - 1) / NT;
+    constexpr int KS = W / 32;    // 18 k-steps of the score contraction
+    constexpr int NU = RK / 16;   // 32 latent column tiles of U^T
+    __shared__ __attribute__((aligned(16))) u16 lds[TT * STRIDE];
+
+    const int p = blockIdx.x, b = blockIdx.y;
+    const int L = clampi(ctx_lens[b], 0, max_ctx);
+    const int t0 = p * chunk;
+    if (t0 >= L) return;
+    const int t1 = min(t0 + chunk, L);
+    const int ntiles = (t1 - t0 + TT - 1) / TT;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int q4 = lane >> 4, r16 = lane & 15;
+    const int RQ = s_q * h_q;
+    const int hpg = h_q / g;
+    const int rho0 = blockIdx.z * (NW * 16) + wave * 16;
+    const bool active = rho0 < RQ;
+    const int rho = rho0 + r16;
+    const bool row_ok = rho < RQ;
+    const int s = row_ok ? rho / h_q : 0;
+    const int h = row_ok ? rho - s * h_q : 0;
+    const int nvis = clampi(L - s_q + s + 1, 0, L);
+
+    bf16x8 qv[KS];
+    const u16* qsrc = qhat + ((size_t)b * RQ + rho) * W + q4 * 8;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) qv[kk] = row_ok ? ld_bf16x8(qsrc + kk * 32) : zero_bf16x8();
+
+    floatx4 uacc[NU];
+#pragma unroll
+    for (int n = 0; n < NU; ++n) uacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    SoftmaxState st{kNegInf, 0.f};
+
+    const u16* seq = cache + (size_t)b * bstride;
+    u32x4 reg[NLOAD];
+    load_tile<W, NT, NLOAD>(reg, seq + (size_t)t0 * W, min(TT, t1 - t0), tid);
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int tb = t0 + it * TT;
+        if (it > 0) __syncthreads();
+        store_tile<W, STRIDE, NT, NLOAD>(lds, reg, tid);
+        __syncthreads();
+        if (it + 1 < ntiles) {
+            const int tn = tb + TT;
+            load_tile<W, NT, NLOAD>(reg, seq + (size_t)tn * W, min(TT, t1 - tn), tid);
+        }
+        if (!active) continue;
+
+        float sc[8];
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            const u16* arow = lds + (th * 16 + r16) * STRIDE + q4 * 8;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) acc = mfma16(ld_bf16x8(arow + kk * 32), qv[kk], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = tb + th * 16 + q4 * 4 + i;
+                sc[th * 4 + i] = (row_ok && t < t1 && t < nvis) ? acc[i] * scale_log2 : kNegInf;
+            }
+        }
+        float alpha;
+        const bf16x8 pb = softmax_tile(st, sc, alpha);
+#pragma unroll
+        for (int n = 0; n < NU; ++n) {
+            uacc[n] *= alpha;
+            uacc[n] = mfma16(gather_col(lds, STRIDE, q4, 16 * n + r16), pb, uacc[n]);
+        }
+    }
+    if (!active) return;
+
+    const float l = wave_sum16x4(st.l);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    // U^T as the B operand of o^T = W_UV[j] U^T: k-step ks covers latent columns
+    // 32ks + slot_token(q4, e), which are uacc[2ks + e/4][e%4] of this lane.
+    bf16x8 ub[RK / 32];
+#pragma unroll
+    for (int ks = 0; ks < RK / 32; ++ks) {
+        u32x4 v;
+        v[0] = pack2f(uacc[2 * ks][0] * inv, uacc[2 * ks][1] * inv);
+        v[1] = pack2f(uacc[2 * ks][2] * inv, uacc[2 * ks][3] * inv);
+        v[2] = pack2f(uacc[2 * ks + 1][0] * inv, uacc[2 * ks + 1][1] * inv);
+        v[3] = pack2f(uacc[2 * ks + 1][2] * inv, uacc[2 * ks + 1][3] * inv);
+        ub[ks] = as_bf16x8(v);
+    }
+    const int jrow = h / hpg;
+    const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
+    // groups of the wave's rows: rows never straddle a query token when h_q % 16 == 0
+    const int last = min(rho0 + 15, RQ - 1);
+    const int jlo = (rho0 % h_q) / hpg, jhi = (last % h_q) / hpg;
+    for (int jj = jlo; jj <= jhi; ++jj) {
+        const u16* wj = w_uv + (size_t)jj * DH * RK;
+#pragma unroll 2
+        for (int mt = 0; mt < DH / 16; ++mt) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            const u16* wrow = wj + (size_t)(mt * 16 + r16) * RK + q4 * 4;
+#pragma unroll
+            for (int ks = 0; ks < RK / 32; ++ks) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(wrow + ks * 32);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(wrow + ks * 32 + 16);
+                acc = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), ub[ks], acc);
+            }
+            if (row_ok && jrow == jj) *reinterpret_cast<floatx4*>(part_o + prow * DH + mt * 16 + q4 * 4) = acc;
+        }
+    }
+    if (row_ok && q4 == 0) part_lse[prow] = l > 0.f ? (st.m + __log2f(l)) * kLn2 : kNegInf;
+}
+
+template <int G, int NW>
+hipError_t launch_gqa_t(const DecodeArgs& a, hipStream_t st) {
+    const int rows_g = a.s_q * (a.h_q / a.g);
+    const int pairs = G * ((rows_g + 15) / 16);
+    dim3 grid(a.n_split, a.batch, (pairs + NW - 1) / NW);
+    hipError_t e = record_if(a.ev_before, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gqa_decode_kernel<G, NW>), grid, dim3(NW * 64), 0, st,
+                       (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.cache, a.bstride,
+                       a.ctx_lens, a.max_ctx, a.h_q, a.s_q, a.chunk, a.batch, a.scale * kLog2e,
+                       a.part_o, a.part_lse);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return record_if(a.ev_after, st);
+}
+
+// 8 waves per block: with 1024-thread blocks the 128-register cap spills the
+// staging registers; extra (group, row tile) pairs go to further blocks in z.
+template <int G>
+hipError_t launch_gqa_g(const DecodeArgs& a, hipStream_t st) {
+    return launch_gqa_t<G, 8>(a, st);
+}
+
+}  // namespace
+
+bool gqa_bf16_supported(int g, int rows_per_group) {
+    return (g == 1 || g == 2 || g == 4 || g == 8) && rows_per_group >= 1;
+}
+
+hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t st) {
+    switch (a.g) {
+        case 1: return launch_gqa_g<1>(a, st);
+        case 2: return launch_gqa_g<2>(a, st);
+        case 4: return launch_gqa_g<4>(a, st);
+        case 8: return launch_gqa_g<8>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st) {
+    const int hpg = a.h_q / a.g;
+    const int rows_per_group = a.batch * a.s_q * hpg;
+    dim3 pgrid((rows_per_group + 63) / 64, a.g);
+    hipLaunchKernelGGL(absorb_prologue_kernel, pgrid, dim3(256), 0, st,
+                       (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.w_uk, (u16*)a.qhat,
+                       a.batch, a.h_q, a.g, a.s_q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int RQ = a.s_q * a.h_q;
+    dim3 grid(a.n_split, a.batch, (RQ + kAbsorbRowsPerBlock - 1) / kAbsorbRowsPerBlock);
+    e = record_if(a.ev_before, st);
+    if (e != hipSuccess) return e;
+    if (RQ >= kAbsorbRowsPerBlock) {
+        hipLaunchKernelGGL(absorb_decode_kernel<8>, grid, dim3(512), 0, st,
+                           (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
+                           a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.batch, a.scale * kLog2e, a.part_o, a.part_lse);
+    } else {
+        // fewer query rows than a full block: 2 waves suffice for up to 32 rows, 4 for 64
+        if (RQ <= 32) {
+            hipLaunchKernelGGL(absorb_decode_kernel<2>, grid, dim3(128), 0, st,
+                               (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
+                               a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.batch, a.scale * kLog2e, a.part_o,
+                               a.part_lse);
+        } else if (RQ <= 64) {
+            hipLaunchKernelGGL(absorb_decode_kernel<4>, grid, dim3(256), 0, st,
+                               (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
+                               a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.batch, a.scale * kLog2e, a.part_o,
+                               a.part_lse);
+        } else {
+            hipLaunchKernelGGL(absorb_decode_kernel<8>, grid, dim3(512), 0, st,
+                               (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
+                               a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.batch, a.scale * kLog2e, a.part_o,
+                               a.part_lse);
+        }
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return record_if(a.ev_after, st);
+}
+
+}  // namespace gqla

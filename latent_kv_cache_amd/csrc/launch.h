@@ -1,0 +1,64 @@
+// Internal interface between the C-ABI host layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqla {
+
+// Everything a decode launch needs, already validated by the host layer.
+struct DecodeArgs {
+    int h_q, g, r_kv, d_r, d_h, s_q;
+    float scale;
+    int batch, max_ctx;
+    int n_split, chunk;                 // context chunks per sequence, tokens per chunk
+    const void* q_nope;
+    const void* q_rope;
+    const void* w_uk;                   // absorb only
+    const void* w_uv;                   // absorb only
+    const void* cache;                  // latent rows (absorb) or expanded rows (GQA)
+    int64_t bstride;                    // elements between sequences of `cache`
+    const int32_t* ctx_lens;
+    void* out;
+    float* lse;                         // nullable
+    float* part_o;                      // [n_split][batch][s_q][h_q][d_h]
+    float* part_lse;                    // [n_split][batch][s_q][h_q]
+    void* qhat;                         // absorb bf16: [batch][s_q*h_q][r_kv+d_r]
+    hipEvent_t ev_before, ev_after;     // optional, recorded around the main attention kernel
+};
+
+inline hipError_t record_if(hipEvent_t ev, hipStream_t st) { return ev ? hipEventRecord(ev, st) : hipSuccess; }
+
+struct ExpandArgs {
+    int h_q, g, r_kv, d_r, d_h;
+    int batch, max_ctx, row_begin;
+    const void* latent;
+    int64_t latent_bstride;
+    const void* w_uk;
+    const void* w_uv;
+    const int32_t* ctx_lens;
+    void* group_cache;
+    int64_t group_bstride;
+};
+
+// bf16 MFMA path (r_kv = 512, d_r = 64, d_h = 128)
+hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_expand_bf16(const ExpandArgs& a, hipStream_t st);
+bool gqa_bf16_supported(int g, int rows_per_group);
+
+// fp32 vector path (generic dims within the documented bounds)
+hipError_t launch_absorb_f32(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_expand_f32(const ExpandArgs& a, hipStream_t st);
+
+// split-K log-sum-exp merge of the per-chunk partials into out / lse
+hipError_t launch_combine(const DecodeArgs& a, bool out_bf16, hipStream_t st);
+
+// tile sizes the planner must respect
+constexpr int kBf16TokenTile = 32;      // chunks are multiples of this on the bf16 path
+constexpr int kF32MaxChunk = 1024;      // scores of one chunk live in LDS on the fp32 path
+constexpr int kAbsorbRowsPerBlock = 128;  // query rows per absorb workgroup (8 waves x 16)
+
+}  // namespace gqla

@@ -1,0 +1,183 @@
+"""ctypes binding of libgqla (include/gqla.h): argument marshalling only.
+
+Every step of the decode path runs in the library's HIP kernels.  Torch is
+used for device memory and the current stream: tensors are passed as raw
+device pointers plus element strides.  There is no fallback: if the built
+library is missing, or a call returns a non-zero status, this module raises.
+
+Method: "GQLA: Group-Query Latent Attention for Hardware-Adaptive LLM
+Decoding", technical summary section 2 (the MQA-absorb and GQA decode paths
+over the same group-indexed up-projections).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgqla.so")
+
+BF16, F32 = 0, 1
+ABSORB, GQA = 0, 1
+STATUS = {0: "GQLA_OK", 1: "GQLA_ERR_INVALID_ARG", 2: "GQLA_ERR_UNSUPPORTED", 3: "GQLA_ERR_WORKSPACE", 4: "GQLA_ERR_HIP"}
+
+EXPORTS = ("gqla_workspace_size", "gqla_plan_splits", "gqla_expand_groups", "gqla_decode_absorb",
+           "gqla_decode_gqa", "gqla_set_kernel_events", "gqla_status_string", "gqla_last_error")
+
+
+class Shape(ctypes.Structure):
+    """Mirror of struct gqla_shape."""
+
+    _fields_ = [("h_q", ctypes.c_int32), ("g", ctypes.c_int32), ("r_kv", ctypes.c_int32),
+                ("d_r", ctypes.c_int32), ("d_h", ctypes.c_int32), ("s_q", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class GQLAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgqla.so (once) and declare its signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m latent_kv_cache_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    # torch first: its bundled HIP runtime then satisfies the library's libamdhip64.so.7
+    # dependency, so device pointers, streams and events are shared with one runtime.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(path)
+    c_i32, c_i64, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    sp = ctypes.POINTER(Shape)
+    lib.gqla_workspace_size.argtypes = [sp, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]
+    lib.gqla_plan_splits.argtypes = [sp, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
+    lib.gqla_expand_groups.argtypes = [sp, c_i32, c_i32, c_vp, c_i64, c_vp, c_vp, c_vp, c_i32, c_vp, c_i64, c_vp]
+    lib.gqla_decode_absorb.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp,
+                                       c_vp, c_sz, c_i32, c_vp]
+    lib.gqla_decode_gqa.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                    c_i32, c_vp]
+    lib.gqla_set_kernel_events.argtypes = [c_vp, c_vp]
+    for name in ("gqla_workspace_size", "gqla_plan_splits", "gqla_expand_groups", "gqla_decode_absorb",
+                 "gqla_decode_gqa", "gqla_set_kernel_events"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.gqla_status_string.argtypes = [ctypes.c_int]
+    lib.gqla_status_string.restype = ctypes.c_char_p
+    lib.gqla_last_error.argtypes = []
+    lib.gqla_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load().gqla_last_error().decode()
+        raise GQLAError(status, msg)
+
+
+def make_shape(h_q: int, g: int, r_kv: int, d_r: int, d_h: int, s_q: int, scale: Optional[float] = None,
+               dtype: int = BF16) -> Shape:
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h + d_r)
+    return Shape(h_q, g, r_kv, d_r, d_h, s_q, scale, dtype)
+
+
+def dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def workspace_size(shape: Shape, path: int, batch: int, max_ctx: int, num_splits: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().gqla_workspace_size(ctypes.byref(shape), path, batch, max_ctx, num_splits, ctypes.byref(n)))
+    return int(n.value)
+
+
+def plan_splits(shape: Shape, path: int, batch: int, max_ctx: int, num_splits: int = 0) -> Tuple[int, int]:
+    n, c = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().gqla_plan_splits(ctypes.byref(shape), path, batch, max_ctx, num_splits, ctypes.byref(n),
+                                   ctypes.byref(c)))
+    return int(n.value), int(c.value)
+
+
+def set_kernel_events(before=None, after=None) -> None:
+    """Record two torch.cuda.Event objects around the main attention kernel of later decode
+    calls on this thread (None, None turns it off).  The events must already exist on the
+    device, i.e. have been recorded once."""
+    b = None if before is None else int(before.cuda_event)
+    a = None if after is None else int(after.cuda_event)
+    _check(load().gqla_set_kernel_events(b, a))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def _rows(t, width: int) -> Tuple[int, int]:
+    """(batch stride in elements, max_ctx) of a [B][S][width] cache tensor with packed rows."""
+    if t.dim() != 3 or t.shape[2] != width or t.stride(2) != 1 or t.stride(1) != width:
+        raise ValueError(f"cache tensor must be [B][S][{width}] with packed rows, got {tuple(t.shape)} "
+                         f"strides {t.stride()}")
+    return int(t.stride(0)), int(t.shape[1])
+
+
+def alloc_workspace(shape: Shape, path: int, batch: int, max_ctx: int, num_splits: int = 0, device=None):
+    import torch
+    n = workspace_size(shape, path, batch, max_ctx, num_splits)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device or "cuda")
+
+
+def expand_groups(shape: Shape, latent, w_uk, w_uv, ctx_lens, group_cache, row_begin: int = 0, stream=None):
+    """Write group rows [row_begin, L_b) of group_cache [B][S][2 g d_h + d_r] from latent [B][S][r_kv + d_r]."""
+    lbs, max_ctx = _rows(latent, shape.r_kv + shape.d_r)
+    gbs, gctx = _rows(group_cache, 2 * shape.g * shape.d_h + shape.d_r)
+    if gctx < max_ctx:
+        raise ValueError("group_cache holds fewer rows per sequence than latent")
+    _check(load().gqla_expand_groups(ctypes.byref(shape), latent.shape[0], max_ctx, _ptr(latent), lbs, _ptr(w_uk),
+                                     _ptr(w_uv), _ptr(ctx_lens), row_begin, _ptr(group_cache), gbs, _stream(stream)))
+
+
+def decode_absorb(shape: Shape, q_nope, q_rope, w_uk, w_uv, latent, ctx_lens, out, lse=None, workspace=None,
+                  num_splits: int = 0, stream=None):
+    """MQA-absorb decode into out [B][s_q][h_q][d_h] (and lse [B][s_q][h_q] if given)."""
+    lbs, max_ctx = _rows(latent, shape.r_kv + shape.d_r)
+    batch = latent.shape[0]
+    if workspace is None:
+        workspace = alloc_workspace(shape, ABSORB, batch, max_ctx, num_splits, latent.device)
+    _check(load().gqla_decode_absorb(ctypes.byref(shape), batch, max_ctx, _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                     _ptr(w_uv), _ptr(latent), lbs, _ptr(ctx_lens), _ptr(out), _ptr(lse),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(), num_splits,
+                                     _stream(stream)))
+    return out
+
+
+def decode_gqa(shape: Shape, q_nope, q_rope, group_cache, ctx_lens, out, lse=None, workspace=None,
+               num_splits: int = 0, stream=None):
+    """GQA decode over expanded rows into out [B][s_q][h_q][d_h] (and lse if given)."""
+    gbs, max_ctx = _rows(group_cache, 2 * shape.g * shape.d_h + shape.d_r)
+    batch = group_cache.shape[0]
+    if workspace is None:
+        workspace = alloc_workspace(shape, GQA, batch, max_ctx, num_splits, group_cache.device)
+    _check(load().gqla_decode_gqa(ctypes.byref(shape), batch, max_ctx, _ptr(q_nope), _ptr(q_rope),
+                                  _ptr(group_cache), gbs, _ptr(ctx_lens), _ptr(out), _ptr(lse), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), num_splits, _stream(stream)))
+    return out

@@ -1,0 +1,199 @@
+"""HIP path vs the fp64 oracle, element by element, through the C-ABI (MI355X only).
+
+Sizes span several 32-token tiles, ragged tails and several split-K chunks at
+shapes the oracle finishes in seconds; the full-size launches (the ones the
+benchmark times) are checked on sampled sequences.  Tolerance: |gpu - oracle|
+<= 2e-3 + 2e-2 |oracle| for bf16 storage, 1e-4 + 1e-4 |oracle| for fp32.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from synth.inputs import sample_sequences
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def note(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def gqla():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    from latent_kv_cache_amd import gqla as mod
+    mod.load()
+    return mod
+
+
+def both_paths(cfg, lens, gqla, num_splits=0, seqs=None, max_ctx=None, what=""):
+    w = gu.workload(cfg, lens=lens, max_ctx=max_ctx)
+    seqs = list(range(cfg.batch)) if seqs is None else seqs
+    note(f"{what} absorb cfg={cfg.name} B={cfg.batch} g={cfg.g} s_q={cfg.s_q} lens={list(w.lens[:6])} splits={num_splits}")
+    out, lse = gu.run_absorb(w, gqla, num_splits)
+    gu.compare(cfg, out, lse, seqs, w.lens, f"{what} absorb")
+    note(f"{what} expand + gqa")
+    gc = gu.expand(w, gqla)
+    out2, lse2 = gu.run_gqa(w, gqla, gc, num_splits)
+    gu.compare(cfg, out2, lse2, seqs, w.lens, f"{what} gqa")
+    return w, (out, lse), (out2, lse2)
+
+
+# ---------------------------------------------------------------- tiny fp32 (config 1, full size)
+@pytest.mark.parametrize("num_splits", [0, 1, 3, 256])
+def test_tiny_fp32(gqla, num_splits):
+    cfg = synth.config(1)
+    both_paths(cfg, None, gqla, num_splits, what="tiny")
+
+
+def test_tiny_fp32_ragged_multi(gqla):
+    cfg = synth.config(1).with_(batch=4, s_q=2)
+    both_paths(cfg, [256, 1, 0, 97], gqla, 2, max_ctx=256, what="tiny-ragged")
+
+
+# ---------------------------------------------------------------- bf16 shapes at reduced batch/context
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_llama3_shape(gqla, num_splits):
+    cfg = synth.config(2).with_(batch=3)
+    both_paths(cfg, [4096, 1000, 33], gqla, num_splits, what="cfg2")
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 5])
+def test_flagship_shape_ragged(gqla, num_splits):
+    cfg = synth.config(3).with_(batch=3)
+    both_paths(cfg, [1000, 8192, 31], gqla, num_splits, max_ctx=8192, what="cfg3")
+
+
+@pytest.mark.parametrize("g,s_q", [(8, 2), (4, 1), (8, 1)])
+def test_multi_token_shapes(gqla, g, s_q):
+    cfg = synth.config(4, g=g, s_q=s_q).with_(batch=4)
+    lens = [int(x) for x in synth.ctx_lens(synth.config(4))[:4]]
+    lens = [min(x, 3000) for x in lens[:3]] + [2]
+    both_paths(cfg, lens, gqla, 0, what=f"cfg4 g{g} s_q{s_q}")
+
+
+def test_absorb_sq2_long(gqla):
+    cfg = synth.config(4, s_q=2).with_(batch=2)
+    w = gu.workload(cfg, lens=[4097, 1])
+    note("absorb s_q=2 lens [4097, 1]")
+    out, lse = gu.run_absorb(w, gqla, 0)
+    gu.compare(cfg, out, lse, [0, 1], w.lens, "absorb sq2")
+
+
+def test_long_context_shape(gqla):
+    cfg = synth.config(5).with_(batch=2)
+    lens = [int(x) for x in synth.ctx_lens(synth.config(5))[:2]]
+    both_paths(cfg, lens, gqla, 0, what="cfg5")
+
+
+# ---------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_edge_lengths(gqla, s_q):
+    """Empty, single-row, shorter-than-s_q and exactly-one-chunk contexts in one batch."""
+    cfg = synth.config(3, s_q=s_q).with_(batch=7)
+    lens = [0, 1, 2, 32, 33, 64, 95]
+    both_paths(cfg, lens, gqla, 3, max_ctx=96, what=f"edges s_q{s_q}")
+
+
+def test_chunk_boundary_causal(gqla):
+    """s_q = 2 with L - 1 on a chunk boundary: query 0 sees nothing of the last chunk."""
+    cfg = synth.config(4, s_q=2).with_(batch=2)
+    # max_ctx 129 in 2 splits -> chunks of 96; L = 97 puts row L - 1 alone in chunk 1
+    both_paths(cfg, [97, 65], gqla, 2, max_ctx=129, what="causal-boundary")
+
+
+# ---------------------------------------------------------------- properties
+def test_split_invariance_and_determinism(gqla):
+    cfg = synth.config(3).with_(batch=2)
+    w = gu.workload(cfg, lens=[3000, 2049])
+    note("split invariance absorb/gqa")
+    a1, _ = gu.run_absorb(w, gqla, 1)
+    a2, _ = gu.run_absorb(w, gqla, 0)
+    a3, _ = gu.run_absorb(w, gqla, 0)
+    assert gu.torch_mod().equal(a2, a3), "absorb is not bitwise deterministic"
+    d = np.abs(gu.host(a1) - gu.host(a2))
+    assert d.max() <= 2e-3 + 2e-2 * np.abs(gu.host(a1)).max()
+    gc = gu.expand(w, gqla)
+    g1, _ = gu.run_gqa(w, gqla, gc, 1)
+    g2, _ = gu.run_gqa(w, gqla, gc, 0)
+    g3, _ = gu.run_gqa(w, gqla, gc, 0)
+    assert gu.torch_mod().equal(g2, g3), "gqa is not bitwise deterministic"
+    # the two paths agree with each other (algebraic equivalence, section 2)
+    dd = np.abs(gu.host(a2) - gu.host(g2))
+    assert np.all(dd <= 4e-3 + 4e-2 * np.abs(gu.host(g2)))
+
+
+def test_expand_matches_oracle(gqla):
+    """Expanded rows equal the fp64 expansion rounded once to bf16 (within one bf16 ulp)."""
+    import oracle
+    cfg = synth.config(3).with_(batch=2)
+    w = gu.workload(cfg, lens=[300, 77], max_ctx=320)
+    note("expand rows")
+    torch = gu.torch_mod()
+    width = 2 * cfg.g * cfg.d_h + cfg.d_r
+    gc = torch.full((2, 320, width), 7.0, dtype=torch.bfloat16, device="cuda")
+    gu.expand(w, gqla, gc, row_begin=0)
+    w_uk, w_uv = synth.up_weights(cfg)
+    gch = gu.host(gc)
+    for b, L in enumerate(w.lens):
+        ref = oracle.expand_groups(synth.latent_rows(cfg, b, int(L)), w_uk, w_uv)
+        got = gch[b, :L].astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6), f"b={b}"
+        assert np.all(gch[b, L:] == 7.0), "rows past L_b were written"
+
+
+def test_expand_row_begin(gqla):
+    """row_begin expands only rows [row_begin, L_b): the decode-step append of s_q new rows."""
+    cfg = synth.config(4, g=4).with_(batch=2)
+    w = gu.workload(cfg, lens=[130, 64], max_ctx=130)
+    torch = gu.torch_mod()
+    full = gu.expand(w, gqla)
+    width = 2 * cfg.g * cfg.d_h + cfg.d_r
+    part = torch.full((2, 130, width), 3.0, dtype=torch.bfloat16, device="cuda")
+    note("expand row_begin=62")
+    gu.expand(w, gqla, part, row_begin=62)
+    fh, ph = gu.host(full), gu.host(part)
+    assert np.all(ph[:, :62] == 3.0)
+    assert np.array_equal(ph[0, 62:130], fh[0, 62:130])
+    assert np.array_equal(ph[1, 62:64], fh[1, 62:64])
+    assert np.all(ph[1, 64:] == 3.0)
+
+
+# ---------------------------------------------------------------- full-size launches, sampled sequences
+@pytest.mark.parametrize("cfg_id", [2, 3])
+def test_full_size_sampled(gqla, cfg_id):
+    cfg = synth.config(cfg_id)
+    seqs = sample_sequences(cfg, 4)
+    both_paths(cfg, None, gqla, 0, seqs=seqs, what=f"full cfg{cfg_id}")
+
+
+def test_full_size_multi_token_sampled(gqla):
+    torch = gu.torch_mod()
+    for g, s_q, paths in ((8, 2, ("gqa", "absorb")), (4, 1, ("gqa",))):
+        cfg = synth.config(4, g=g, s_q=s_q)
+        seqs = sample_sequences(cfg, 3)
+        w = gu.workload(cfg)
+        if "absorb" in paths:
+            note(f"full cfg4 absorb s_q={s_q}")
+            out, lse = gu.run_absorb(w, gqla, 0)
+            gu.compare(cfg, out, lse, seqs, w.lens, "full cfg4 absorb")
+            del out, lse
+        note(f"full cfg4 gqa g={g} s_q={s_q}")
+        gc = gu.expand(w, gqla)
+        out, lse = gu.run_gqa(w, gqla, gc, 0)
+        gu.compare(cfg, out, lse, seqs, w.lens, f"full cfg4 gqa g{g}")
+        del gc, out, lse, w
+        torch.cuda.empty_cache()
+
+
+def test_full_size_long_context_sampled(gqla):
+    cfg = synth.config(5)
+    both_paths(cfg, None, gqla, 0, seqs=[0, 15], what="full cfg5")
+
+
+if __name__ == "__main__":  # pragma: no cover
+    sys.exit(pytest.main([__file__, "-v"]))
