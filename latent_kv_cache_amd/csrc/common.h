@@ -11,6 +11,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -40,6 +41,38 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() { return as_bf16x8(u32x4{0u, 0u,
 __device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+// Same lane layout with fp16 operands.  The decode kernels keep bf16 in HBM but feed
+// the MFMA fp16: its 10-bit mantissa keeps the absorbed query and the softmax weights
+// P eight times closer to their fp32 values than bf16 would, at the same MFMA rate.
+__device__ __forceinline__ floatx4 mfma16h(f16x8 a, f16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+__device__ __forceinline__ f16x8 ld_f16x8(const u16* p) {
+    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ f16x8 zero_f16x8() { return as_f16x8(u32x4{0u, 0u, 0u, 0u}); }
+
+// Two packed bf16 -> two packed fp16.  Exact for magnitudes in [2^-14, 65504]; smaller
+// values lose low bits (fp16 subnormals), larger ones saturate (round toward zero).
+__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t v) {
+    const float lo = __uint_as_float(v << 16);
+    const float hi = __uint_as_float(v & 0xffff0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+__device__ __forceinline__ u32x4 bf8_to_h8(u32x4 v) {
+    return u32x4{bf2_to_h2(v[0]), bf2_to_h2(v[1]), bf2_to_h2(v[2]), bf2_to_h2(v[3])};
+}
+
+// fp32 -> fp16, round to nearest even.
+__device__ __forceinline__ u16 f2h(float f) { return __builtin_bit_cast(u16, (_Float16)f); }
+
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) { return pack2(f2h(lo), f2h(hi)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

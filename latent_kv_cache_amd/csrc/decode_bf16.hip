@@ -14,6 +14,10 @@
 // one contiguous span of HBM (rows of a sequence are packed), loaded with
 // 16-byte vector loads into registers one tile ahead and stored into LDS with
 // a 16-byte pad per row, which makes the MFMA operand reads bank-conflict free.
+// HBM holds bf16; the tile is converted to fp16 on its way into LDS (exact for
+// bf16 values within fp16's range) and the contractions run on fp16 MFMA, so the
+// absorbed query and the softmax weights P, which the kernel itself rounds, keep
+// 10 mantissa bits instead of 7.
 // Each wave owns 16 query rows (the M = 16 side of the 16x16x32 MFMA: the 16
 // heads of a group on the GQA path at h_q/g = 16, or 16 of the heads sharing
 // the latent on the absorb path) and keeps its queries and accumulators in
@@ -46,7 +50,7 @@ struct SoftmaxState {
     float l;   // lane-partial running sum of exp2
 };
 
-__device__ __forceinline__ bf16x8 softmax_tile(SoftmaxState& st, float (&sc)[8], float& alpha) {
+__device__ __forceinline__ f16x8 softmax_tile(SoftmaxState& st, float (&sc)[8], float& alpha) {
     float mt = sc[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
@@ -64,16 +68,16 @@ __device__ __forceinline__ bf16x8 softmax_tile(SoftmaxState& st, float (&sc)[8],
     st.l = st.l * alpha + ps;
     st.m = mnew;
     u32x4 pk;
-    pk[0] = pack2f(p[0], p[1]);
-    pk[1] = pack2f(p[2], p[3]);
-    pk[2] = pack2f(p[4], p[5]);
-    pk[3] = pack2f(p[6], p[7]);
-    return as_bf16x8(pk);
+    pk[0] = pack2h(p[0], p[1]);
+    pk[1] = pack2h(p[2], p[3]);
+    pk[2] = pack2h(p[4], p[5]);
+    pk[3] = pack2h(p[6], p[7]);
+    return as_f16x8(pk);
 }
 
 // A operand of O^T += V^T P^T: lane (q4, r16) needs column `col` of the tile at the
 // eight slot tokens.
-__device__ __forceinline__ bf16x8 gather_col(const u16* lds, int stride, int q4, int col) {
+__device__ __forceinline__ f16x8 gather_col(const u16* lds, int stride, int q4, int col) {
     u32x4 v;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -81,7 +85,7 @@ __device__ __forceinline__ bf16x8 gather_col(const u16* lds, int stride, int q4,
         const u16 hi = lds[slot_token(q4, 2 * h + 1) * stride + col];
         v[h] = pack2(lo, hi);
     }
-    return as_bf16x8(v);
+    return as_f16x8(v);
 }
 
 // Copy rows [row0, row0 + nrows) of a packed row-major span (width W elements) into
@@ -101,6 +105,7 @@ __device__ __forceinline__ void load_tile(u32x4 (&reg)[NLOAD], const u16* __rest
     }
 }
 
+// Store the staged tile into LDS as fp16 (bf16 -> fp16 conversion per element).
 template <int W, int STRIDE, int NT, int NLOAD>
 __device__ __forceinline__ void store_tile(u16* lds, const u32x4 (&reg)[NLOAD], int tid) {
     constexpr int CPR = W / 8;
@@ -110,7 +115,7 @@ __device__ __forceinline__ void store_tile(u16* lds, const u32x4 (&reg)[NLOAD], 
         if (c < TT * CPR) {
             const int r = c / CPR;
             const int col = c - r * CPR;
-            *reinterpret_cast<u32x4*>(lds + r * STRIDE + col * 8) = reg[k];
+            *reinterpret_cast<u32x4*>(lds + r * STRIDE + col * 8) = bf8_to_h8(reg[k]);
         }
     }
 }
@@ -158,14 +163,15 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
     const int qrow = (b * s_q + s) * h_q + h;
 
     // queries as the B operand of S^T = K Q^T: k-steps 0..3 over q^N, 4..5 over q^R
-    bf16x8 qv[6];
+    f16x8 qv[6];
 #pragma unroll
     for (int kk = 0; kk < 6; ++kk) {
         if (row_ok) {
-            qv[kk] = kk < 4 ? ld_bf16x8(q_nope + (size_t)qrow * DH + kk * 32 + q4 * 8)
-                            : ld_bf16x8(q_rope + (size_t)qrow * DR + (kk - 4) * 32 + q4 * 8);
+            const u16* src = kk < 4 ? q_nope + (size_t)qrow * DH + kk * 32 + q4 * 8
+                                    : q_rope + (size_t)qrow * DR + (kk - 4) * 32 + q4 * 8;
+            qv[kk] = as_f16x8(bf8_to_h8(*reinterpret_cast<const u32x4*>(src)));
         } else {
-            qv[kk] = zero_bf16x8();
+            qv[kk] = zero_f16x8();
         }
     }
 
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
 #pragma unroll
             for (int kk = 0; kk < 6; ++kk) {
                 const int col = kk < 4 ? j * DH + kk * 32 + q4 * 8 : 2 * G * DH + (kk - 4) * 32 + q4 * 8;
-                acc = mfma16(ld_bf16x8(arow + col), qv[kk], acc);
+                acc = mfma16h(ld_f16x8(arow + col), qv[kk], acc);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -206,12 +212,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
             }
         }
         float alpha;
-        const bf16x8 pb = softmax_tile(st, sc, alpha);
+        const f16x8 pb = softmax_tile(st, sc, alpha);
         const int vcol = (G + j) * DH + r16;
 #pragma unroll
         for (int n = 0; n < DH / 16; ++n) {
             oacc[n] *= alpha;
-            oacc[n] = mfma16(gather_col(lds, STRIDE, q4, vcol + 16 * n), pb, oacc[n]);
+            oacc[n] = mfma16h(gather_col(lds, STRIDE, q4, vcol + 16 * n), pb, oacc[n]);
         }
     }
     if (!row_ok) return;
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
 
 // ---------------------------------------------------------------------------
 // Absorb prologue: qhat[b][rho][0:512] = W_UK[j]^T q^N, qhat[b][rho][512:576] = q^R,
-// rho = s*h_q + h.  grid = (row blocks of 64, g); block = 4 waves.  The rows of
+// rho = s*h_q + h, stored as fp16 (the operand type of the decode kernel's MFMA).  grid = (row blocks of 64, g); block = 4 waves.  The rows of
 // group j are numbered iota = (b*s_q + s)*hpg + hh.  W_UK[j] is staged in LDS
 // transposed ([r][d]) so the contraction over d reads 16 contiguous bytes.
 // ---------------------------------------------------------------------------
@@ -284,8 +290,8 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
         }
         if (ok) {
             u32x2 o;
-            o[0] = pack2f(acc[0], acc[1]);
-            o[1] = pack2f(acc[2], acc[3]);
+            o[0] = pack2h(acc[0], acc[1]);
+            o[1] = pack2h(acc[2], acc[3]);
             *reinterpret_cast<u32x2*>(dst + mt * 16 + q4 * 4) = o;
         }
     }
@@ -294,7 +300,8 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int off = (q4 + 4 * c) * 8;
-            *reinterpret_cast<u32x4*>(dst + RK + off) = *reinterpret_cast<const u32x4*>(q_rope + qrow * DR + off);
+            *reinterpret_cast<u32x4*>(dst + RK + off) =
+                bf8_to_h8(*reinterpret_cast<const u32x4*>(q_rope + qrow * DR + off));
         }
     }
 }
@@ -340,10 +347,10 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     const int h = row_ok ? rho - s * h_q : 0;
     const int nvis = clampi(L - s_q + s + 1, 0, L);
 
-    bf16x8 qv[KS];
+    f16x8 qv[KS];
     const u16* qsrc = qhat + ((size_t)b * RQ + rho) * W + q4 * 8;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qv[kk] = row_ok ? ld_bf16x8(qsrc + kk * 32) : zero_bf16x8();
+    for (int kk = 0; kk < KS; ++kk) qv[kk] = row_ok ? ld_f16x8(qsrc + kk * 32) : zero_f16x8();
 
     floatx4 uacc[NU];
 #pragma unroll
@@ -371,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
             const u16* arow = lds + (th * 16 + r16) * STRIDE + q4 * 8;
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) acc = mfma16(ld_bf16x8(arow + kk * 32), qv[kk], acc);
+            for (int kk = 0; kk < KS; ++kk) acc = mfma16h(ld_f16x8(arow + kk * 32), qv[kk], acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = tb + th * 16 + q4 * 4 + i;
@@ -379,11 +386,11 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
             }
         }
         float alpha;
-        const bf16x8 pb = softmax_tile(st, sc, alpha);
+        const f16x8 pb = softmax_tile(st, sc, alpha);
 #pragma unroll
         for (int n = 0; n < NU; ++n) {
             uacc[n] *= alpha;
-            uacc[n] = mfma16(gather_col(lds, STRIDE, q4, 16 * n + r16), pb, uacc[n]);
+            uacc[n] = mfma16h(gather_col(lds, STRIDE, q4, 16 * n + r16), pb, uacc[n]);
         }
     }
     if (!active) return;
@@ -391,16 +398,23 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     const float l = wave_sum16x4(st.l);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     // U^T as the B operand of o^T = W_UV[j] U^T: k-step ks covers latent columns
-    // 32ks + slot_token(q4, e), which are uacc[2ks + e/4][e%4] of this lane.
-    bf16x8 ub[RK / 32];
+    // 32ks + slot_token(q4, e), which are uacc[2ks + e/4][e%4] of this lane.  u is
+    // split into two bf16 terms (u = hi + lo to about 16 bits) so that W_UV, which is
+    // bf16, multiplies it with no rounding of u beyond fp32's.
+    bf16x8 ub[RK / 32], ul[RK / 32];
 #pragma unroll
     for (int ks = 0; ks < RK / 32; ++ks) {
-        u32x4 v;
-        v[0] = pack2f(uacc[2 * ks][0] * inv, uacc[2 * ks][1] * inv);
-        v[1] = pack2f(uacc[2 * ks][2] * inv, uacc[2 * ks][3] * inv);
-        v[2] = pack2f(uacc[2 * ks + 1][0] * inv, uacc[2 * ks + 1][1] * inv);
-        v[3] = pack2f(uacc[2 * ks + 1][2] * inv, uacc[2 * ks + 1][3] * inv);
-        ub[ks] = as_bf16x8(v);
+        u32x4 vh, vl;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const floatx4& src = uacc[2 * ks + (h >> 1)];
+            const float a = src[2 * (h & 1)] * inv, c = src[2 * (h & 1) + 1] * inv;
+            const u16 ah = f2bf(a), ch = f2bf(c);
+            vh[h] = pack2(ah, ch);
+            vl[h] = pack2f(a - bf2f(ah), c - bf2f(ch));
+        }
+        ub[ks] = as_bf16x8(vh);
+        ul[ks] = as_bf16x8(vl);
     }
     const int jrow = h / hpg;
     const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
@@ -417,7 +431,9 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
             for (int ks = 0; ks < RK / 32; ++ks) {
                 const u32x2 lo = *reinterpret_cast<const u32x2*>(wrow + ks * 32);
                 const u32x2 hi = *reinterpret_cast<const u32x2*>(wrow + ks * 32 + 16);
-                acc = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), ub[ks], acc);
+                const bf16x8 wa = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                acc = mfma16(wa, ub[ks], acc);
+                acc = mfma16(wa, ul[ks], acc);
             }
             if (row_ok && jrow == jj) *reinterpret_cast<floatx4*>(part_o + prow * DH + mt * 16 + q4 * 4) = acc;
         }

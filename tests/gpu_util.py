@@ -76,15 +76,51 @@ def oracle_seq(cfg, b, length, q_nope, q_rope, w_uk, w_uv):
     return oracle.textbook_decode(rows, q_nope[b], q_rope[b], w_uk, w_uv, length, cfg.scale)
 
 
-def compare(cfg, out, lse, seqs, lens, what=""):
-    """Element-wise comparison of device outputs against the oracle on the listed sequences."""
+def stored_group_rows(cfg, b, length):
+    """The oracle's fp64 expansion of sequence b rounded once to the storage dtype:
+    the rows a group cache holds, [L][2 g d_h + d_R] float32."""
+    w_uk, w_uv = synth.up_weights(cfg)
+    gr = oracle.expand_groups(synth.latent_rows(cfg, b, length), w_uk, w_uv)
+    return synth.bf16_round(gr) if cfg.dtype == "bf16" else gr.astype(np.float32)
+
+
+def upload_stored_group_cache(w):
+    """Device group cache [B][max_ctx][width] holding stored_group_rows of every sequence."""
+    torch = torch_mod()
+    cfg = w.cfg
+    width = 2 * cfg.g * cfg.d_h + cfg.d_r
+    gc = torch.zeros((cfg.batch, w.max_ctx, width), dtype=w.dtype, device=w.latent.device)
+    rows = {}
+    for b in range(cfg.batch):
+        L = int(w.lens[b])
+        rows[b] = stored_group_rows(cfg, b, L)
+        if L:
+            gc[b, :L].copy_(torch.from_numpy(rows[b]).to(w.dtype))
+    return gc, rows
+
+
+def gqa_reference(cfg, rows):
+    """Reference of the GQA decode entry point: the oracle's GQA form over the stored rows."""
+    qn, qr = synth.queries(cfg)
+
+    def ref(b, length):
+        return oracle.gqa_decode(rows[b], qn[b], qr[b], cfg.g, length, cfg.scale)
+    return ref
+
+
+def compare(cfg, out, lse, seqs, lens, what="", ref=None):
+    """Element-wise comparison of device outputs against the oracle on the listed sequences.
+    ref(b, L) -> (o, lse) overrides the default reference (the textbook definition)."""
     rtol, atol = TOL[cfg.dtype]
     qn, qr = synth.queries(cfg)
     w_uk, w_uv = synth.up_weights(cfg)
     o_dev, l_dev = host(out), host(lse)
     worst = 0.0
     for b in seqs:
-        o_ref, l_ref = oracle_seq(cfg, b, int(lens[b]), qn, qr, w_uk, w_uv)
+        if ref is None:
+            o_ref, l_ref = oracle_seq(cfg, b, int(lens[b]), qn, qr, w_uk, w_uv)
+        else:
+            o_ref, l_ref = ref(b, int(lens[b]))
         got = o_dev[b].astype(np.float64)
         assert np.all(np.isfinite(got)), f"{what} b={b}: non-finite output"
         err = np.abs(got - o_ref)

@@ -4,6 +4,15 @@ Sizes span several 32-token tiles, ragged tails and several split-K chunks at
 shapes the oracle finishes in seconds; the full-size launches (the ones the
 benchmark times) are checked on sampled sequences.  Tolerance: |gpu - oracle|
 <= 2e-3 + 2e-2 |oracle| for bf16 storage, 1e-4 + 1e-4 |oracle| for fp32.
+
+References.  The absorb decode reads the latent rows themselves, so it is
+compared with the textbook definition at every length.  The GQA decode reads
+an expanded cache that is itself stored in bf16; its reference is the oracle's
+GQA form over those stored rows (the oracle's fp64 expansion rounded once to
+the storage dtype), uploaded as its input.  The expansion kernel is checked
+against the same stored rows, and the whole expand-then-decode chain against
+the textbook definition at the workloads' context lengths (>= 1024 tokens,
+where the rounding of the stored K/V averages out far below the tolerance).
 """
 import sys
 
@@ -30,16 +39,24 @@ def gqla():
     return mod
 
 
-def both_paths(cfg, lens, gqla, num_splits=0, seqs=None, max_ctx=None, what=""):
+def both_paths(cfg, lens, gqla, num_splits=0, seqs=None, max_ctx=None, what="", end_to_end=False):
+    """Absorb decode vs the textbook oracle; GQA decode vs the oracle's GQA form over
+    stored rows (end_to_end: device expansion, then GQA decode vs the textbook)."""
     w = gu.workload(cfg, lens=lens, max_ctx=max_ctx)
     seqs = list(range(cfg.batch)) if seqs is None else seqs
     note(f"{what} absorb cfg={cfg.name} B={cfg.batch} g={cfg.g} s_q={cfg.s_q} lens={list(w.lens[:6])} splits={num_splits}")
     out, lse = gu.run_absorb(w, gqla, num_splits)
     gu.compare(cfg, out, lse, seqs, w.lens, f"{what} absorb")
-    note(f"{what} expand + gqa")
-    gc = gu.expand(w, gqla)
+    if end_to_end:
+        note(f"{what} device expand + gqa vs textbook")
+        gc = gu.expand(w, gqla)
+        ref = None
+    else:
+        note(f"{what} gqa over stored rows")
+        gc, rows = gu.upload_stored_group_cache(w)
+        ref = gu.gqa_reference(cfg, rows)
     out2, lse2 = gu.run_gqa(w, gqla, gc, num_splits)
-    gu.compare(cfg, out2, lse2, seqs, w.lens, f"{what} gqa")
+    gu.compare(cfg, out2, lse2, seqs, w.lens, f"{what} gqa", ref=ref)
     return w, (out, lse), (out2, lse2)
 
 
@@ -87,7 +104,7 @@ def test_absorb_sq2_long(gqla):
 def test_long_context_shape(gqla):
     cfg = synth.config(5).with_(batch=2)
     lens = [int(x) for x in synth.ctx_lens(synth.config(5))[:2]]
-    both_paths(cfg, lens, gqla, 0, what="cfg5")
+    both_paths(cfg, lens, gqla, 0, what="cfg5", end_to_end=True)
 
 
 # ---------------------------------------------------------------- edge cases
@@ -122,14 +139,14 @@ def test_split_invariance_and_determinism(gqla):
     g2, _ = gu.run_gqa(w, gqla, gc, 0)
     g3, _ = gu.run_gqa(w, gqla, gc, 0)
     assert gu.torch_mod().equal(g2, g3), "gqa is not bitwise deterministic"
-    # the two paths agree with each other (algebraic equivalence, section 2)
+    # the two paths agree with each other (algebraic equivalence, section 2); the GQA
+    # side reads bf16-stored K/V, hence twice the tolerance
     dd = np.abs(gu.host(a2) - gu.host(g2))
     assert np.all(dd <= 4e-3 + 4e-2 * np.abs(gu.host(g2)))
 
 
 def test_expand_matches_oracle(gqla):
     """Expanded rows equal the fp64 expansion rounded once to bf16 (within one bf16 ulp)."""
-    import oracle
     cfg = synth.config(3).with_(batch=2)
     w = gu.workload(cfg, lens=[300, 77], max_ctx=320)
     note("expand rows")
@@ -137,12 +154,14 @@ def test_expand_matches_oracle(gqla):
     width = 2 * cfg.g * cfg.d_h + cfg.d_r
     gc = torch.full((2, 320, width), 7.0, dtype=torch.bfloat16, device="cuda")
     gu.expand(w, gqla, gc, row_begin=0)
-    w_uk, w_uv = synth.up_weights(cfg)
     gch = gu.host(gc)
     for b, L in enumerate(w.lens):
-        ref = oracle.expand_groups(synth.latent_rows(cfg, b, int(L)), w_uk, w_uv)
+        stored = gu.stored_group_rows(cfg, b, int(L)).astype(np.float64)
         got = gch[b, :L].astype(np.float64)
-        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6), f"b={b}"
+        # equal to the once-rounded oracle value, or one bf16 ulp away where fp32
+        # accumulation lands on the other side of a rounding boundary
+        assert np.all(np.abs(got - stored) <= 2.0 ** -7 * np.abs(stored) + 1e-30), f"b={b}"
+        assert np.mean(got == stored) > 0.99, f"b={b}: {np.mean(got == stored):.4f} exact"
         assert np.all(gch[b, L:] == 7.0), "rows past L_b were written"
 
 
@@ -168,7 +187,7 @@ def test_expand_row_begin(gqla):
 def test_full_size_sampled(gqla, cfg_id):
     cfg = synth.config(cfg_id)
     seqs = sample_sequences(cfg, 4)
-    both_paths(cfg, None, gqla, 0, seqs=seqs, what=f"full cfg{cfg_id}")
+    both_paths(cfg, None, gqla, 0, seqs=seqs, what=f"full cfg{cfg_id}", end_to_end=True)
 
 
 def test_full_size_multi_token_sampled(gqla):
@@ -192,7 +211,7 @@ def test_full_size_multi_token_sampled(gqla):
 
 def test_full_size_long_context_sampled(gqla):
     cfg = synth.config(5)
-    both_paths(cfg, None, gqla, 0, seqs=[0, 15], what="full cfg5")
+    both_paths(cfg, None, gqla, 0, seqs=[0, 15], what="full cfg5", end_to_end=True)
 
 
 if __name__ == "__main__":  # pragma: no cover
