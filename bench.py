@@ -87,7 +87,7 @@ def cpu_baseline(cfg, budget_s, gpu_out):
     qn, qr = synth.queries(cfg)
     w_uk, w_uv = synth.up_weights(cfg)
     spent, n, worst = 0.0, 0, 0.0
-    for b in sample_sequences(cfg, 8):
+    for b in sample_sequences(cfg, cfg.batch):
         L = synth.ctx_len(cfg, b)
         rows = synth.latent_rows(cfg, b, L)
         t0 = time.perf_counter()
@@ -218,7 +218,7 @@ def main(argv=None):
                 "main_kernel": kernel, "main_kernel_ms": round(kern_ms, 4),
                 "n_split": splits[0], "chunk": splits[1]}
 
-    paths = {"absorb": path_rec(work_a, call_a, kern_a, split_a, "absorb_decode_kernel<8>"),
+    paths = {"absorb": path_rec(work_a, call_a, kern_a, split_a, "absorb_decode_kernel<4>"),
              "gqa": path_rec(work_g, call_g, kern_g, split_g, "gqa_decode_kernel<8, 8>")}
 
     # dominant kernel: the longer of the two main attention kernels
@@ -238,7 +238,7 @@ def main(argv=None):
         achieved = alg / (kern_a * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                 "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("absorb_decode", digest),
-                "kernel": "absorb_decode_kernel<8>", "alg_bytes_per_launch": alg, "avg_ms": round(kern_a, 4)}
+                "kernel": "absorb_decode_kernel<4>", "alg_bytes_per_launch": alg, "avg_ms": round(kern_a, 4)}
 
     cpu, parity = (None, None) if args.no_cpu_baseline else cpu_baseline(
         cfg, args.cpu_seconds, {"absorb": out_a, "gqa": out_g})

@@ -74,6 +74,19 @@ __device__ __forceinline__ u16 f2h(float f) { return __builtin_bit_cast(u16, (_F
 
 __device__ __forceinline__ uint32_t pack2h(float lo, float hi) { return pack2(f2h(lo), f2h(hi)); }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16, gfx950).  Every lane addresses 8 bytes
+// (4 halfwords).  Within each group of 16 lanes, result lane j, element e is element
+// j%4 of what lane 4e + j/4 of the group addressed.  So if the 16 lanes of a group
+// address 4 consecutive columns of 4 rows (lane m: row m/4, columns 4(m%4)..+3), lane
+// j receives column j of those 4 rows: a 4 x 16 block read as its transpose.
+__device__ __forceinline__ u32x2 lds_read_tr16(const u16* p) {
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_max16x4(float v) {

@@ -42,22 +42,37 @@ constexpr int TT = 32;    // tokens per tile
 // 16-token halves of S^T.
 __device__ __forceinline__ int slot_token(int q, int e) { return 16 * (e >> 2) + 4 * q + (e & 3); }
 
-// Online-softmax update for one tile.  sc[e] are raw scores for slot_token(q4, e);
-// masked slots must hold -inf.  Returns P as the bf16 B operand and the factor
-// alpha by which the running accumulators must be rescaled.
+// Online softmax with a lazily raised reference.  Exponentials are taken against a
+// per-row reference m (log2 domain) that is raised only when a tile's maximum exceeds
+// it by more than kLazy; otherwise p = 2^(s - m) <= 2^kLazy, which fp16 P and fp32
+// sums hold as precisely as values <= 1.  When no row of the wave raises its
+// reference, the accumulators need no rescaling for that tile.  The final
+// normalisation and log-sum-exp use the same reference, so the result is that of
+// the exact softmax.
+constexpr float kLazy = 8.f;
+
 struct SoftmaxState {
-    float m;   // running max (log2 domain), identical in the 4 lanes of a row
-    float l;   // lane-partial running sum of exp2
+    float m;   // reference (log2 domain), identical in the 4 lanes of a row; -inf before any row
+    float l;   // lane-partial running sum of 2^(s - m)
 };
 
-__device__ __forceinline__ f16x8 softmax_tile(SoftmaxState& st, float (&sc)[8], float& alpha) {
+// sc[e] are log2-scaled scores for slot_token(q4, e), masked slots -inf.  Returns P as
+// the fp16 B operand; sets rescale (wave-uniform) and alpha when accumulators must be
+// multiplied by alpha before this tile's P is added.
+__device__ __forceinline__ f16x8 softmax_tile(SoftmaxState& st, float (&sc)[8], bool& rescale, float& alpha) {
     float mt = sc[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
     mt = wave_max16x4(mt);
-    const float mnew = fmaxf(st.m, mt);
-    const float muse = (mnew == kNegInf) ? 0.f : mnew;
-    alpha = fast_exp2(st.m - muse);
+    const bool raise = mt > st.m + kLazy;        // false while the row has seen nothing
+    rescale = __any(raise);
+    alpha = 1.f;
+    if (raise) {
+        alpha = fast_exp2(st.m - mt);            // st.m = -inf gives 0
+        st.l *= alpha;
+        st.m = mt;
+    }
+    const float muse = (st.m == kNegInf) ? 0.f : st.m;
     float p[8];
     float ps = 0.f;
 #pragma unroll
@@ -65,8 +80,7 @@ __device__ __forceinline__ f16x8 softmax_tile(SoftmaxState& st, float (&sc)[8], 
         p[e] = fast_exp2(sc[e] - muse);
         ps += p[e];
     }
-    st.l = st.l * alpha + ps;
-    st.m = mnew;
+    st.l += ps;
     u32x4 pk;
     pk[0] = pack2h(p[0], p[1]);
     pk[1] = pack2h(p[2], p[3]);
@@ -75,17 +89,15 @@ __device__ __forceinline__ f16x8 softmax_tile(SoftmaxState& st, float (&sc)[8], 
     return as_f16x8(pk);
 }
 
-// A operand of O^T += V^T P^T: lane (q4, r16) needs column `col` of the tile at the
-// eight slot tokens.
-__device__ __forceinline__ f16x8 gather_col(const u16* lds, int stride, int q4, int col) {
-    u32x4 v;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        const u16 lo = lds[slot_token(q4, 2 * h) * stride + col];
-        const u16 hi = lds[slot_token(q4, 2 * h + 1) * stride + col];
-        v[h] = pack2(lo, hi);
-    }
-    return as_f16x8(v);
+// A operand of O^T += V^T P^T: lane (q4, r16) needs column col0 + r16 of the tile at
+// the eight slot tokens 4q4 + e and 16 + 4q4 + e (e = 0..3).  Lane m of the 16-lane
+// group addresses row 4q4 + m/4 (then 16 rows further), columns col0 + 4(m%4)..+3;
+// the transposing read hands lane j column col0 + j of those rows.
+__device__ __forceinline__ f16x8 gather_col(const u16* lds, int stride, int q4, int r16, int col0) {
+    const u16* p0 = lds + (4 * q4 + (r16 >> 2)) * stride + col0 + 4 * (r16 & 3);
+    const u32x2 lo = lds_read_tr16(p0);
+    const u32x2 hi = lds_read_tr16(p0 + 16 * stride);
+    return as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 // Copy rows [row0, row0 + nrows) of a packed row-major span (width W elements) into
@@ -196,29 +208,38 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
         if (!active) continue;
 
         float sc[8];
-#pragma unroll
-        for (int th = 0; th < 2; ++th) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            const u16* arow = lds + (th * 16 + r16) * STRIDE;
+        {
+            // two independent accumulator chains per 16-token half
+            floatx4 acc[2][2] = {};
 #pragma unroll
             for (int kk = 0; kk < 6; ++kk) {
                 const int col = kk < 4 ? j * DH + kk * 32 + q4 * 8 : 2 * G * DH + (kk - 4) * 32 + q4 * 8;
-                acc = mfma16h(ld_f16x8(arow + col), qv[kk], acc);
+#pragma unroll
+                for (int th = 0; th < 2; ++th)
+                    acc[th][kk & 1] = mfma16h(ld_f16x8(lds + (th * 16 + r16) * STRIDE + col), qv[kk], acc[th][kk & 1]);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = tb + th * 16 + q4 * 4 + i;
-                sc[th * 4 + i] = (row_ok && t < t1 && t < nvis) ? acc[i] * scale_log2 : kNegInf;
+            for (int th = 0; th < 2; ++th) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tb + th * 16 + q4 * 4 + i;
+                    const float v = acc[th][0][i] + acc[th][1][i];
+                    sc[th * 4 + i] = (row_ok && t < t1 && t < nvis) ? v * scale_log2 : kNegInf;
+                }
             }
         }
+        bool rescale;
         float alpha;
-        const f16x8 pb = softmax_tile(st, sc, alpha);
-        const int vcol = (G + j) * DH + r16;
+        const f16x8 pb = softmax_tile(st, sc, rescale, alpha);
+        if (__builtin_expect(rescale, 0)) {
+            asm volatile("" ::: "memory");
 #pragma unroll
-        for (int n = 0; n < DH / 16; ++n) {
-            oacc[n] *= alpha;
-            oacc[n] = mfma16h(gather_col(lds, STRIDE, q4, vcol + 16 * n), pb, oacc[n]);
+            for (int n = 0; n < DH / 16; ++n) oacc[n] *= alpha;
         }
+        const int vcol = (G + j) * DH;
+#pragma unroll
+        for (int n = 0; n < DH / 16; ++n)
+            oacc[n] = mfma16h(gather_col(lds, STRIDE, q4, r16, vcol + 16 * n), pb, oacc[n]);
     }
     if (!row_ok) return;
 
@@ -235,33 +256,28 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
 
 // ---------------------------------------------------------------------------
 // Absorb prologue: qhat[b][rho][0:512] = W_UK[j]^T q^N, qhat[b][rho][512:576] = q^R,
-// rho = s*h_q + h, stored as fp16 (the operand type of the decode kernel's MFMA).  grid = (row blocks of 64, g); block = 4 waves.  The rows of
-// group j are numbered iota = (b*s_q + s)*hpg + hh.  W_UK[j] is staged in LDS
-// transposed ([r][d]) so the contraction over d reads 16 contiguous bytes.
+// rho = s*h_q + h, stored as fp16 (the operand type of the decode kernel's MFMA).
+// grid = (row blocks of 64, g); block = 4 waves.  The rows of group j are numbered
+// iota = (b*s_q + s)*hpg + hh.  W_UK[j] ([d][r], 128 KB) is staged row-major in LDS;
+// the contraction runs over d, so the A operand (W_UK^T) is formed with transposing
+// LDS reads: 4 rows d x 16 columns r per 16-lane group.
 // ---------------------------------------------------------------------------
-constexpr int PRO_STRIDE = DH + 8;
+constexpr int PRO_STRIDE = RK + 8;
 
 __global__ __launch_bounds__(256) void absorb_prologue_kernel(
     const u16* __restrict__ q_nope, const u16* __restrict__ q_rope, const u16* __restrict__ w_uk,
     u16* __restrict__ qhat, int batch, int h_q, int g, int s_q) {
-    __shared__ __attribute__((aligned(16))) u16 wt[RK * PRO_STRIDE];
+    __shared__ __attribute__((aligned(16))) u16 wt[DH * PRO_STRIDE];
     const int j = blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int q4 = lane >> 4, r16 = lane & 15;
 
     const u16* wj = w_uk + (size_t)j * DH * RK;
-    // 128 x 512 -> transposed; chunk c: d = c % 128, r8 = c / 128 (consecutive lanes write
-    // consecutive d, i.e. consecutive LDS halfwords)
     for (int c = tid; c < DH * (RK / 8); c += 256) {
-        const int d = c & (DH - 1);
-        const int r8 = c >> 7;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(wj + (size_t)d * RK + r8 * 8);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            wt[(r8 * 8 + 2 * h) * PRO_STRIDE + d] = (u16)(v[h] & 0xffffu);
-            wt[(r8 * 8 + 2 * h + 1) * PRO_STRIDE + d] = (u16)(v[h] >> 16);
-        }
+        const int d = c >> 6, r8 = c & 63;
+        *reinterpret_cast<u32x4*>(wt + d * PRO_STRIDE + r8 * 8) =
+            *reinterpret_cast<const u32x4*>(wj + (size_t)d * RK + r8 * 8);
     }
     __syncthreads();
 
@@ -281,12 +297,17 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
 #pragma unroll
     for (int kd = 0; kd < DH / 32; ++kd) qb[kd] = ok ? ld_bf16x8(q_nope + qrow * DH + kd * 32 + q4 * 8) : zero_bf16x8();
 
+    // A operand lane (q4, r16), k-step kd: W_UK[32kd + 8q4 + e][16mt + r16], e = 0..7
+    const u16* abase = wt + (8 * q4 + (r16 >> 2)) * PRO_STRIDE + 4 * (r16 & 3);
 #pragma unroll 4
     for (int mt = 0; mt < RK / 16; ++mt) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kd = 0; kd < DH / 32; ++kd) {
-            acc = mfma16(ld_bf16x8(wt + (mt * 16 + r16) * PRO_STRIDE + kd * 32 + q4 * 8), qb[kd], acc);
+            const u16* pa = abase + kd * 32 * PRO_STRIDE + mt * 16;
+            const u32x2 lo = lds_read_tr16(pa);
+            const u32x2 hi = lds_read_tr16(pa + 4 * PRO_STRIDE);
+            acc = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), qb[kd], acc);
         }
         if (ok) {
             u32x2 o;
@@ -307,17 +328,23 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Absorb latent attention with fused W_UV.  grid = (n_split, batch, row blocks of
-// 128); block = NW waves; wave w owns query rows rho = z*128 + 16w + (0..15) of the
+// Absorb latent attention with fused W_UV.  Block = NW waves (one per SIMD, so each
+// wave may hold 512 registers: 72 for its queries, 128 for u, the rest for staging
+// and operand prefetch); wave w owns query rows rho = z*16NW + 16w + (0..15) of the
 // s_q*h_q rows (rho = s*h_q + h), all attending to the shared 576-wide rows.
 // After the chunk, u = P.C / l stays in registers and each group present in the
 // wave's rows applies W_UV[j] with MFMA, so the partial written is o_p (d_h wide).
+//
+// One-dimensional grid, XCD-aware.  Workgroups are dealt round-robin to the 8 XCDs
+// (block id mod 8), each with its own L2.  The nz row blocks of one (chunk,
+// sequence) pair read the same cache rows, so they get block ids 8 apart: same XCD,
+// dispatched back to back, and the second read of every row is an L2 hit.
 // ---------------------------------------------------------------------------
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     const u16* __restrict__ qhat, const u16* __restrict__ w_uv,
     const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
-    int max_ctx, int h_q, int g, int s_q, int chunk, int batch, float scale_log2,
+    int max_ctx, int h_q, int g, int s_q, int chunk, int n_split, int nz, int batch, float scale_log2,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
     constexpr int W = RK + DR;
     constexpr int STRIDE = W + 8;
@@ -327,7 +354,11 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     constexpr int NU = RK / 16;   // 32 latent column tiles of U^T
     __shared__ __attribute__((aligned(16))) u16 lds[TT * STRIDE];
 
-    const int p = blockIdx.x, b = blockIdx.y;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int z = slot % nz;
+    const int pair = (slot / nz) * 8 + xcd;
+    if (pair >= n_split * batch) return;           // padding of the last group of 8
+    const int b = pair / n_split, p = pair - b * n_split;
     const int L = clampi(ctx_lens[b], 0, max_ctx);
     const int t0 = p * chunk;
     if (t0 >= L) return;
@@ -339,7 +370,7 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     const int q4 = lane >> 4, r16 = lane & 15;
     const int RQ = s_q * h_q;
     const int hpg = h_q / g;
-    const int rho0 = blockIdx.z * (NW * 16) + wave * 16;
+    const int rho0 = z * (NW * 16) + wave * 16;
     const bool active = rho0 < RQ;
     const int rho = rho0 + r16;
     const bool row_ok = rho < RQ;
@@ -373,25 +404,38 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
         if (!active) continue;
 
         float sc[8];
+        {
+            // two independent accumulator chains per 16-token half
+            floatx4 acc[2][2] = {};
+            const u16* arow = lds + r16 * STRIDE + q4 * 8;
 #pragma unroll
-        for (int th = 0; th < 2; ++th) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            const u16* arow = lds + (th * 16 + r16) * STRIDE + q4 * 8;
+            for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) acc = mfma16h(ld_f16x8(arow + kk * 32), qv[kk], acc);
+                for (int th = 0; th < 2; ++th)
+                    acc[th][kk & 1] = mfma16h(ld_f16x8(arow + th * 16 * STRIDE + kk * 32), qv[kk], acc[th][kk & 1]);
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = tb + th * 16 + q4 * 4 + i;
-                sc[th * 4 + i] = (row_ok && t < t1 && t < nvis) ? acc[i] * scale_log2 : kNegInf;
+            for (int th = 0; th < 2; ++th) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tb + th * 16 + q4 * 4 + i;
+                    const float v = acc[th][0][i] + acc[th][1][i];
+                    sc[th * 4 + i] = (row_ok && t < t1 && t < nvis) ? v * scale_log2 : kNegInf;
+                }
             }
         }
+        bool rescale;
         float alpha;
-        const f16x8 pb = softmax_tile(st, sc, alpha);
+        const f16x8 pb = softmax_tile(st, sc, rescale, alpha);
+        if (__builtin_expect(rescale, 0)) {
+            // rare (the reference rose by more than kLazy); kept as a real branch so the
+            // accumulators are not touched by VALU on the common path
+            asm volatile("" ::: "memory");
 #pragma unroll
-        for (int n = 0; n < NU; ++n) {
-            uacc[n] *= alpha;
-            uacc[n] = mfma16h(gather_col(lds, STRIDE, q4, 16 * n + r16), pb, uacc[n]);
+            for (int n = 0; n < NU; ++n) uacc[n] *= alpha;
         }
+#pragma unroll
+        for (int n = 0; n < NU; ++n) uacc[n] = mfma16h(gather_col(lds, STRIDE, q4, r16, 16 * n), pb, uacc[n]);
     }
     if (!active) return;
 
@@ -466,6 +510,8 @@ hipError_t launch_gqa_g(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
+int absorb_waves(int query_rows) { return query_rows <= 32 ? 2 : 4; }
+
 bool gqa_bf16_supported(int g, int rows_per_group) {
     return (g == 1 || g == 2 || g == 4 || g == 8) && rows_per_group >= 1;
 }
@@ -490,31 +536,22 @@ hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int RQ = a.s_q * a.h_q;
-    dim3 grid(a.n_split, a.batch, (RQ + kAbsorbRowsPerBlock - 1) / kAbsorbRowsPerBlock);
+    const int nw = absorb_waves(RQ);
+    const int nz = (RQ + 16 * nw - 1) / (16 * nw);
+    const int pairs = a.n_split * a.batch;
+    dim3 grid(((pairs + 7) / 8) * 8 * nz);
     e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;
-    if (RQ >= kAbsorbRowsPerBlock) {
-        hipLaunchKernelGGL(absorb_decode_kernel<8>, grid, dim3(512), 0, st,
+    if (nw == 2) {
+        hipLaunchKernelGGL(absorb_decode_kernel<2>, grid, dim3(128), 0, st,
                            (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
-                           a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.batch, a.scale * kLog2e, a.part_o, a.part_lse);
+                           a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e,
+                           a.part_o, a.part_lse);
     } else {
-        // fewer query rows than a full block: 2 waves suffice for up to 32 rows, 4 for 64
-        if (RQ <= 32) {
-            hipLaunchKernelGGL(absorb_decode_kernel<2>, grid, dim3(128), 0, st,
-                               (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
-                               a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.batch, a.scale * kLog2e, a.part_o,
-                               a.part_lse);
-        } else if (RQ <= 64) {
-            hipLaunchKernelGGL(absorb_decode_kernel<4>, grid, dim3(256), 0, st,
-                               (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
-                               a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.batch, a.scale * kLog2e, a.part_o,
-                               a.part_lse);
-        } else {
-            hipLaunchKernelGGL(absorb_decode_kernel<8>, grid, dim3(512), 0, st,
-                               (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
-                               a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.batch, a.scale * kLog2e, a.part_o,
-                               a.part_lse);
-        }
+        hipLaunchKernelGGL(absorb_decode_kernel<4>, grid, dim3(256), 0, st,
+                           (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
+                           a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e,
+                           a.part_o, a.part_lse);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -47,6 +47,7 @@ hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_expand_bf16(const ExpandArgs& a, hipStream_t st);
 bool gqa_bf16_supported(int g, int rows_per_group);
+int absorb_waves(int query_rows);          // waves (16 query rows each) per absorb workgroup
 
 // fp32 vector path (generic dims within the documented bounds)
 hipError_t launch_absorb_f32(const DecodeArgs& a, hipStream_t st);
@@ -59,6 +60,5 @@ hipError_t launch_combine(const DecodeArgs& a, bool out_bf16, hipStream_t st);
 // tile sizes the planner must respect
 constexpr int kBf16TokenTile = 32;      // chunks are multiples of this on the bf16 path
 constexpr int kF32MaxChunk = 1024;      // scores of one chunk live in LDS on the fp32 path
-constexpr int kAbsorbRowsPerBlock = 128;  // query rows per absorb workgroup (8 waves x 16)
 
 }  // namespace gqla

@@ -159,8 +159,10 @@ def test_expand_matches_oracle(gqla):
         stored = gu.stored_group_rows(cfg, b, int(L)).astype(np.float64)
         got = gch[b, :L].astype(np.float64)
         # equal to the once-rounded oracle value, or one bf16 ulp away where fp32
-        # accumulation lands on the other side of a rounding boundary
-        assert np.all(np.abs(got - stored) <= 2.0 ** -7 * np.abs(stored) + 1e-30), f"b={b}"
+        # accumulation lands on the other side of a rounding boundary; the absolute
+        # term covers fp32 accumulation of 512 products (|sum of terms| ~ 20) where
+        # cancellation leaves a value far smaller than its terms
+        assert np.all(np.abs(got - stored) <= 2.0 ** -7 * np.abs(stored) + 1e-4), f"b={b}"
         assert np.mean(got == stored) > 0.99, f"b={b}: {np.mean(got == stored):.4f} exact"
         assert np.all(gch[b, L:] == 7.0), "rows past L_b were written"
 
