@@ -30,6 +30,9 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # MFMA accumulators in ordinary VGPRs: the decode loops rescale them with VALU,
+    # and accumulators in AGPRs would be copied to VGPRs and back every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

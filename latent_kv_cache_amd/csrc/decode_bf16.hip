@@ -13,7 +13,10 @@
 // Tiling.  A workgroup streams its chunk in tiles of 32 cache rows.  A tile is
 // one contiguous span of HBM (rows of a sequence are packed), loaded with
 // 16-byte vector loads into registers one tile ahead and stored into LDS with
-// a 16-byte pad per row, which makes the MFMA operand reads bank-conflict free.
+// a 32-byte pad per row.  On gfx950 a row stride of 8 x (odd) dwords modulo the 64
+// LDS banks lets the 16-byte operand reads of 16 rows, and the transposing reads of
+// 4 rows x 32 bytes, proceed at close to the full LDS rate (a 16-byte pad, 36 dwords
+// mod 64, measured at about 60 % of it).
 // HBM holds bf16; the tile is converted to fp16 on its way into LDS (exact for
 // bf16 values within fp16's range) and the contractions run on fp16 MFMA, so the
 // absorbed query and the softmax weights P, which the kernel itself rounds, keep
@@ -49,7 +52,7 @@ __device__ __forceinline__ int slot_token(int q, int e) { return 16 * (e >> 2) +
 // reference, the accumulators need no rescaling for that tile.  The final
 // normalisation and log-sum-exp use the same reference, so the result is that of
 // the exact softmax.
-constexpr float kLazy = 8.f;
+constexpr float kLazy = 10.f;
 
 struct SoftmaxState {
     float m;   // reference (log2 domain), identical in the 4 lanes of a row; -inf before any row
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
     int max_ctx, int h_q, int s_q, int chunk, int batch, float scale_log2,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
     constexpr int W = 2 * G * DH + DR;
-    constexpr int STRIDE = W + 8;
+    constexpr int STRIDE = W + 16;   // row stride = 8 x odd dwords mod 64 banks
     constexpr int NT = NW * 64;
     constexpr int NLOAD = (TT * (W / 8) + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) u16 lds[TT * STRIDE];
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
 // the contraction runs over d, so the A operand (W_UK^T) is formed with transposing
 // LDS reads: 4 rows d x 16 columns r per 16-lane group.
 // ---------------------------------------------------------------------------
-constexpr int PRO_STRIDE = RK + 8;
+constexpr int PRO_STRIDE = RK + 16;
 
 __global__ __launch_bounds__(256) void absorb_prologue_kernel(
     const u16* __restrict__ q_nope, const u16* __restrict__ q_rope, const u16* __restrict__ w_uk,
@@ -328,10 +331,12 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Absorb latent attention with fused W_UV.  Block = NW waves (one per SIMD, so each
-// wave may hold 512 registers: 72 for its queries, 128 for u, the rest for staging
-// and operand prefetch); wave w owns query rows rho = z*16NW + 16w + (0..15) of the
-// s_q*h_q rows (rho = s*h_q + h), all attending to the shared 576-wide rows.
+// Absorb latent attention with fused W_UV.  Block = NW waves (one per SIMD: each
+// wave keeps 128 registers of u plus staging and operand prefetch); wave w owns
+// query rows rho = z*16NW + 16w + (0..15) of the s_q*h_q rows (rho = s*h_q + h),
+// all attending to the shared 576-wide rows.  The block's absorbed queries (16NW
+// rows of 576 fp16) sit in LDS next to the tile and are read as the B operand of
+// the scores, which leaves the registers to the prefetch of MFMA operands.
 // After the chunk, u = P.C / l stays in registers and each group present in the
 // wave's rows applies W_UV[j] with MFMA, so the partial written is o_p (d_h wide).
 //
@@ -341,18 +346,24 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
 // dispatched back to back, and the second read of every row is an L2 hit.
 // ---------------------------------------------------------------------------
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
+__global__ __launch_bounds__((NW + 4) * 64) void absorb_decode_kernel(
     const u16* __restrict__ qhat, const u16* __restrict__ w_uv,
     const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
     int max_ctx, int h_q, int g, int s_q, int chunk, int n_split, int nz, int batch, float scale_log2,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
     constexpr int W = RK + DR;
-    constexpr int STRIDE = W + 8;
-    constexpr int NT = NW * 64;
-    constexpr int NLOAD = (TT * (W / 8) + NT - 1) / NT;
-    constexpr int KS = W / 32;    // 18 k-steps of the score contraction
-    constexpr int NU = RK / 16;   // 32 latent column tiles of U^T
-    __shared__ __attribute__((aligned(16))) u16 lds[TT * STRIDE];
+    constexpr int STRIDE = W + 16;   // row stride = 8 x odd dwords mod 64 banks
+    constexpr int KS = W / 32;        // 18 k-steps of the score contraction
+    constexpr int NU = RK / 16;       // 32 latent column tiles of U^T
+    constexpr int QROWS = NW * 16;
+    constexpr int TILE = TT * STRIDE; // elements of one LDS tile buffer
+    constexpr int NP = 4;             // producer waves
+    constexpr int PT = NP * 64;
+    constexpr int CPR = W / 8;        // 16-byte chunks per row
+    constexpr int PL = (TT * CPR + PT - 1) / PT;   // chunks per producer thread per tile
+    constexpr int DEPTH = 3;          // tiles a producer thread keeps in flight
+    __shared__ __attribute__((aligned(16))) u16 buf[2 * TILE];
+    __shared__ __attribute__((aligned(16))) u16 qs[QROWS * STRIDE];
 
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int z = slot % nz;
@@ -367,52 +378,90 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int q4 = lane >> 4, r16 = lane & 15;
     const int RQ = s_q * h_q;
+
+    // the block's absorbed query rows -> LDS (rows past s_q*h_q are zero); made
+    // visible to the consumers by the first tile barrier
+    {
+        const int qrow0 = z * QROWS;
+        const u16* qsrc = qhat + ((size_t)b * RQ + qrow0) * W;
+        for (int c = tid; c < QROWS * CPR; c += (NW + NP) * 64) {
+            const int r = c / CPR, col = c - r * CPR;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (qrow0 + r < RQ) v = *reinterpret_cast<const u32x4*>(qsrc + (size_t)r * W + col * 8);
+            *reinterpret_cast<u32x4*>(qs + r * STRIDE + col * 8) = v;
+        }
+    }
+
+    const u16* seq = cache + (size_t)b * bstride + (size_t)t0 * W;
+    if (wave >= NW) {
+        // ---------------- producer waves: HBM -> registers -> fp16 -> LDS, DEPTH tiles ahead.
+        // Tile it is stored into buf[it & 1] before barrier it; the consumers read it after
+        // that barrier and are done with it before barrier it + 1, so buf[it & 1] is free
+        // again when the producers store tile it + 2 after barrier it + 1.
+        const int ptid = tid - NW * 64;
+        u32x4 stage[DEPTH][PL];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d)
+            if (d < ntiles) load_tile<W, PT, PL>(stage[d], seq + (size_t)d * TT * W, min(TT, t1 - t0 - d * TT), ptid);
+        for (int it0 = 0; it0 < ntiles; it0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int it = it0 + d;
+                if (it < ntiles) {
+                    store_tile<W, STRIDE, PT, PL>(buf + (it & 1) * TILE, stage[d], ptid);
+                    const int tn = it + DEPTH;
+                    if (tn < ntiles) load_tile<W, PT, PL>(stage[d], seq + (size_t)tn * TT * W, min(TT, t1 - t0 - tn * TT), ptid);
+                    __syncthreads();
+                }
+            }
+        }
+        return;
+    }
+
+    // ---------------- consumer waves
+    const int q4 = lane >> 4, r16 = lane & 15;
     const int hpg = h_q / g;
-    const int rho0 = z * (NW * 16) + wave * 16;
+    const int rho0 = z * QROWS + wave * 16;
     const bool active = rho0 < RQ;
     const int rho = rho0 + r16;
     const bool row_ok = rho < RQ;
     const int s = row_ok ? rho / h_q : 0;
     const int h = row_ok ? rho - s * h_q : 0;
     const int nvis = clampi(L - s_q + s + 1, 0, L);
-
-    f16x8 qv[KS];
-    const u16* qsrc = qhat + ((size_t)b * RQ + rho) * W + q4 * 8;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qv[kk] = row_ok ? ld_f16x8(qsrc + kk * 32) : zero_f16x8();
+    const u16* qrow_lds = qs + (wave * 16 + r16) * STRIDE + q4 * 8;
 
     floatx4 uacc[NU];
 #pragma unroll
     for (int n = 0; n < NU; ++n) uacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
     SoftmaxState st{kNegInf, 0.f};
 
-    const u16* seq = cache + (size_t)b * bstride;
-    u32x4 reg[NLOAD];
-    load_tile<W, NT, NLOAD>(reg, seq + (size_t)t0 * W, min(TT, t1 - t0), tid);
-
     for (int it = 0; it < ntiles; ++it) {
         const int tb = t0 + it * TT;
-        if (it > 0) __syncthreads();
-        store_tile<W, STRIDE, NT, NLOAD>(lds, reg, tid);
         __syncthreads();
-        if (it + 1 < ntiles) {
-            const int tn = tb + TT;
-            load_tile<W, NT, NLOAD>(reg, seq + (size_t)tn * W, min(TT, t1 - tn), tid);
-        }
         if (!active) continue;
+        const u16* lds = buf + (it & 1) * TILE;
 
         float sc[8];
         {
-            // two independent accumulator chains per 16-token half
+            // two independent accumulator chains per 16-token half; the operands of
+            // k-step kk+1 are read from LDS before the MFMAs of k-step kk are issued
             floatx4 acc[2][2] = {};
             const u16* arow = lds + r16 * STRIDE + q4 * 8;
+            f16x8 a0 = ld_f16x8(arow), a1 = ld_f16x8(arow + 16 * STRIDE), bq = ld_f16x8(qrow_lds);
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-                for (int th = 0; th < 2; ++th)
-                    acc[th][kk & 1] = mfma16h(ld_f16x8(arow + th * 16 * STRIDE + kk * 32), qv[kk], acc[th][kk & 1]);
+                f16x8 n0 = a0, n1 = a1, nb = bq;
+                if (kk + 1 < KS) {
+                    n0 = ld_f16x8(arow + (kk + 1) * 32);
+                    n1 = ld_f16x8(arow + 16 * STRIDE + (kk + 1) * 32);
+                    nb = ld_f16x8(qrow_lds + (kk + 1) * 32);
+                }
+                acc[0][kk & 1] = mfma16h(a0, bq, acc[0][kk & 1]);
+                acc[1][kk & 1] = mfma16h(a1, bq, acc[1][kk & 1]);
+                a0 = n0;
+                a1 = n1;
+                bq = nb;
             }
 #pragma unroll
             for (int th = 0; th < 2; ++th) {
@@ -434,8 +483,18 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
 #pragma unroll
             for (int n = 0; n < NU; ++n) uacc[n] *= alpha;
         }
+        {
+            // PV with the A operand of column tile n+2 read ahead of MFMA n
+            f16x8 c0 = gather_col(lds, STRIDE, q4, r16, 0), c1 = gather_col(lds, STRIDE, q4, r16, 16);
 #pragma unroll
-        for (int n = 0; n < NU; ++n) uacc[n] = mfma16h(gather_col(lds, STRIDE, q4, r16, 16 * n), pb, uacc[n]);
+            for (int n = 0; n < NU; ++n) {
+                f16x8 c2 = c0;
+                if (n + 2 < NU) c2 = gather_col(lds, STRIDE, q4, r16, 16 * (n + 2));
+                uacc[n] = mfma16h(c0, pb, uacc[n]);
+                c0 = c1;
+                c1 = c2;
+            }
+        }
     }
     if (!active) return;
 
@@ -543,12 +602,12 @@ hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st) {
     e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;
     if (nw == 2) {
-        hipLaunchKernelGGL(absorb_decode_kernel<2>, grid, dim3(128), 0, st,
+        hipLaunchKernelGGL(absorb_decode_kernel<2>, grid, dim3(6 * 64), 0, st,
                            (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
                            a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e,
                            a.part_o, a.part_lse);
     } else {
-        hipLaunchKernelGGL(absorb_decode_kernel<4>, grid, dim3(256), 0, st,
+        hipLaunchKernelGGL(absorb_decode_kernel<4>, grid, dim3(8 * 64), 0, st,
                            (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
                            a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e,
                            a.part_o, a.part_lse);

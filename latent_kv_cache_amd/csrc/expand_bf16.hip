@@ -11,7 +11,7 @@
 // Tiling.  grid = (2g d_h / 128 column blocks, token chunks, batch).  Each of the
 // 8 waves of a block owns 16 output columns and keeps their 16 x 512 weight rows
 // in registers as the MFMA A operand for the whole chunk; 64-token latent tiles
-// are staged in LDS (16-byte row pad, conflict-free) and read as the B operand.
+// are staged in LDS (32-byte row pad, bank-conflict free) and read as the B operand.
 //   out^T[col][token] = W[col][r] . c^T[r][token]
 // so lane (q, r16) ends with 4 consecutive columns of token r16: one 8-byte store.
 #include "common.h"
@@ -23,7 +23,7 @@ namespace {
 
 constexpr int DH = 128, DR = 64, RK = 512;
 constexpr int XT = 64;                  // tokens per tile
-constexpr int XSTRIDE = RK + 8;         // LDS row stride of a staged latent tile
+constexpr int XSTRIDE = RK + 16;        // LDS row stride of a staged latent tile (8 x odd dwords mod 64)
 constexpr int XTOK_PER_BLOCK = 256;     // tokens per block (4 tiles)
 
 template <int G>
