@@ -218,7 +218,9 @@ def main(argv=None):
                 "main_kernel": kernel, "main_kernel_ms": round(kern_ms, 4),
                 "n_split": splits[0], "chunk": splits[1]}
 
-    paths = {"absorb": path_rec(work_a, call_a, kern_a, split_a, "absorb_decode_kernel<4>"),
+    rq = cfg.s_q * cfg.h_q
+    absorb_name = "absorb_decode_kernel<%d>" % (2 if rq <= 32 else (4 if rq <= 64 else 8))
+    paths = {"absorb": path_rec(work_a, call_a, kern_a, split_a, absorb_name),
              "gqa": path_rec(work_g, call_g, kern_g, split_g, "gqa_decode_kernel<8, 8>")}
 
     # dominant kernel: the longer of the two main attention kernels
@@ -238,7 +240,7 @@ def main(argv=None):
         achieved = alg / (kern_a * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                 "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("absorb_decode", digest),
-                "kernel": "absorb_decode_kernel<4>", "alg_bytes_per_launch": alg, "avg_ms": round(kern_a, 4)}
+                "kernel": absorb_name, "alg_bytes_per_launch": alg, "avg_ms": round(kern_a, 4)}
 
     cpu, parity = (None, None) if args.no_cpu_baseline else cpu_baseline(
         cfg, args.cpu_seconds, {"absorb": out_a, "gqa": out_g})

@@ -331,39 +331,82 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Absorb latent attention with fused W_UV.  Block = NW waves (one per SIMD: each
-// wave keeps 128 registers of u plus staging and operand prefetch); wave w owns
-// query rows rho = z*16NW + 16w + (0..15) of the s_q*h_q rows (rho = s*h_q + h),
-// all attending to the shared 576-wide rows.  The block's absorbed queries (16NW
-// rows of 576 fp16) sit in LDS next to the tile and are read as the B operand of
-// the scores, which leaves the registers to the prefetch of MFMA operands.
+// Absorb latent attention with fused W_UV.  Block = NW waves of 16 query rows each
+// (rho = z*16NW + 16w + (0..15) of the s_q*h_q rows, rho = s*h_q + h), all
+// attending to the shared 576-wide rows; each wave keeps its absorbed queries (72
+// registers) and u (128 registers) for the whole chunk.
+//
+// Tiles of 32 rows reach LDS by direct global->LDS loads (global_load_lds_dwordx4:
+// lane l of a wave instruction lands at base + 16 l), three buffers deep, so two
+// tiles are in flight while one is computed and no registers stage data.  Buffer
+// slot s (16 bytes) is row s / SROW, column chunk s % SROW of a padded row-major
+// tile; pad slots, slots of rows past the chunk and the spare tail slots receive a
+// dummy in-bounds chunk.  Each wave issues exactly NDMA loads per tile, so waiting
+// for vmcnt <= NDMA (vmcnt 0 on the last tile) means its part of the tile has landed.
+// After a barrier the block converts the tile to fp16 in place (zeroing rows past
+// the chunk), and after a second barrier it computes.
+//
 // After the chunk, u = P.C / l stays in registers and each group present in the
 // wave's rows applies W_UV[j] with MFMA, so the partial written is o_p (d_h wide).
 //
-// One-dimensional grid, XCD-aware.  Workgroups are dealt round-robin to the 8 XCDs
-// (block id mod 8), each with its own L2.  The nz row blocks of one (chunk,
-// sequence) pair read the same cache rows, so they get block ids 8 apart: same XCD,
-// dispatched back to back, and the second read of every row is an L2 hit.
+// One-dimensional grid, XCD-aware: when s_q*h_q needs nz > 1 blocks per (chunk,
+// sequence), the nz blocks get ids 8 apart (same XCD, dispatched back to back), so
+// the second read of every row is an L2 hit.
 // ---------------------------------------------------------------------------
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane l's
+// bytes land at LDS byte address lds_base + 16 l; lds_base must be wave-uniform.  It is
+// issued from inline assembly so that the compiler, which cannot tell which LDS bytes
+// such a load writes, does not wait for all of them before every later LDS access;
+// callers wait with wait_vmcnt<> before reading the destination.  All compiler-visible
+// global loads of a kernel that uses it must be issued before it or waited for by an
+// explicit wait_vmcnt<0>, since the compiler does not count these loads.
+// The global address is a wave-uniform 64-bit base (SGPRs) plus a 32-bit per-lane byte
+// offset, so a lane spends one VGPR on it.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt immediate on gfx9: vmcnt = bits [3:0] and [15:14]; expcnt and
+    // lgkmcnt fields left at their maxima (no wait on them)
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int NW>
-__global__ __launch_bounds__((NW + 4) * 64) void absorb_decode_kernel(
+__global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     const u16* __restrict__ qhat, const u16* __restrict__ w_uv,
     const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
     int max_ctx, int h_q, int g, int s_q, int chunk, int n_split, int nz, int batch, float scale_log2,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
     constexpr int W = RK + DR;
-    constexpr int STRIDE = W + 16;   // row stride = 8 x odd dwords mod 64 banks
+    constexpr int STRIDE = W + 16;    // row stride = 8 x odd dwords mod 64 banks
+    constexpr int SROW = STRIDE / 8;  // 16-byte slots per LDS row (72 data + 2 pad)
+    constexpr int CPR = W / 8;        // data slots per row
     constexpr int KS = W / 32;        // 18 k-steps of the score contraction
     constexpr int NU = RK / 16;       // 32 latent column tiles of U^T
-    constexpr int QROWS = NW * 16;
-    constexpr int TILE = TT * STRIDE; // elements of one LDS tile buffer
-    constexpr int NP = 4;             // producer waves
-    constexpr int PT = NP * 64;
-    constexpr int CPR = W / 8;        // 16-byte chunks per row
-    constexpr int PL = (TT * CPR + PT - 1) / PT;   // chunks per producer thread per tile
-    constexpr int DEPTH = 3;          // tiles a producer thread keeps in flight
-    __shared__ __attribute__((aligned(16))) u16 buf[2 * TILE];
-    __shared__ __attribute__((aligned(16))) u16 qs[QROWS * STRIDE];
+    constexpr int NT = NW * 64;
+    constexpr int TSLOTS = TT * SROW;                  // slots of a tile
+    constexpr int NDMA = (TSLOTS + NT - 1) / NT;       // DMA instructions per wave per tile
+    constexpr int BSLOTS = NDMA * NT;                  // slots of a buffer (spare tail included)
+    constexpr int NBUF = 3;
+    constexpr int KL = RK / 32;                        // 16 latent k-steps: q~ in registers
+    constexpr int QRS = DR + 16;                       // LDS row stride of the rotary queries
+    // three separately declared buffers: with the tile loop unrolled by three every
+    // access names a fixed buffer, so the compiler can tell that reading one buffer
+    // does not depend on the direct loads still landing in the others
+    __shared__ __attribute__((aligned(16))) u16 buf0[BSLOTS * 8];
+    __shared__ __attribute__((aligned(16))) u16 buf1[BSLOTS * 8];
+    __shared__ __attribute__((aligned(16))) u16 buf2[BSLOTS * 8];
+    __shared__ __attribute__((aligned(16))) u16 qr_lds[NW * 16 * QRS];
 
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int z = slot % nz;
@@ -378,123 +421,148 @@ __global__ __launch_bounds__((NW + 4) * 64) void absorb_decode_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int RQ = s_q * h_q;
-
-    // the block's absorbed query rows -> LDS (rows past s_q*h_q are zero); made
-    // visible to the consumers by the first tile barrier
-    {
-        const int qrow0 = z * QROWS;
-        const u16* qsrc = qhat + ((size_t)b * RQ + qrow0) * W;
-        for (int c = tid; c < QROWS * CPR; c += (NW + NP) * 64) {
-            const int r = c / CPR, col = c - r * CPR;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (qrow0 + r < RQ) v = *reinterpret_cast<const u32x4*>(qsrc + (size_t)r * W + col * 8);
-            *reinterpret_cast<u32x4*>(qs + r * STRIDE + col * 8) = v;
-        }
-    }
-
-    const u16* seq = cache + (size_t)b * bstride + (size_t)t0 * W;
-    if (wave >= NW) {
-        // ---------------- producer waves: HBM -> registers -> fp16 -> LDS, DEPTH tiles ahead.
-        // Tile it is stored into buf[it & 1] before barrier it; the consumers read it after
-        // that barrier and are done with it before barrier it + 1, so buf[it & 1] is free
-        // again when the producers store tile it + 2 after barrier it + 1.
-        const int ptid = tid - NW * 64;
-        u32x4 stage[DEPTH][PL];
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d)
-            if (d < ntiles) load_tile<W, PT, PL>(stage[d], seq + (size_t)d * TT * W, min(TT, t1 - t0 - d * TT), ptid);
-        for (int it0 = 0; it0 < ntiles; it0 += DEPTH) {
-#pragma unroll
-            for (int d = 0; d < DEPTH; ++d) {
-                const int it = it0 + d;
-                if (it < ntiles) {
-                    store_tile<W, STRIDE, PT, PL>(buf + (it & 1) * TILE, stage[d], ptid);
-                    const int tn = it + DEPTH;
-                    if (tn < ntiles) load_tile<W, PT, PL>(stage[d], seq + (size_t)tn * TT * W, min(TT, t1 - t0 - tn * TT), ptid);
-                    __syncthreads();
-                }
-            }
-        }
-        return;
-    }
-
-    // ---------------- consumer waves
     const int q4 = lane >> 4, r16 = lane & 15;
+    const int RQ = s_q * h_q;
     const int hpg = h_q / g;
-    const int rho0 = z * QROWS + wave * 16;
+    const int rho0 = z * (NW * 16) + wave * 16;
     const bool active = rho0 < RQ;
     const int rho = rho0 + r16;
     const bool row_ok = rho < RQ;
     const int s = row_ok ? rho / h_q : 0;
     const int h = row_ok ? rho - s * h_q : 0;
     const int nvis = clampi(L - s_q + s + 1, 0, L);
-    const u16* qrow_lds = qs + (wave * 16 + r16) * STRIDE + q4 * 8;
+
+    const u16* seq = cache + (size_t)b * bstride + (size_t)t0 * W;
+    // byte offset within a tile of the chunk each of this lane's DMA slots carries
+    // (-1: pad or spare slot, which receives the tile's first chunk as a dummy)
+    int dma_off[NDMA];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+        const int sl = (i * NW + wave) * 64 + lane;
+        const int r = sl / SROW, c = sl - r * SROW;
+        dma_off[i] = (sl < TSLOTS && c < CPR) ? (r * W + c * 8) * 2 : -1;
+    }
+    // issue the direct loads of tile `it` into the buffer at LDS byte address tbuf
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    auto dma_tile = [&](int it, uint32_t tbuf) {
+        const u16* tsrc = seq + (size_t)it * TT * W;
+        const int lim = min(TT, t1 - t0 - it * TT) * W * 2;   // rows past the chunk: dummy
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const uint32_t off = (dma_off[i] >= 0 && dma_off[i] < lim) ? (uint32_t)dma_off[i] : 0u;
+            dma16(tsrc, off, tbuf + (uint32_t)((i * NW + wave_s) * 1024));
+        }
+    };
+
+    // absorbed latent queries in registers; the 64 rotary columns of the block's rows
+    // in LDS (read twice per tile), made visible by the first tile barrier
+    f16x8 qv[KL];
+    const u16* qsrc = qhat + ((size_t)b * RQ + rho) * W + q4 * 8;
+#pragma unroll
+    for (int kk = 0; kk < KL; ++kk) qv[kk] = row_ok ? ld_f16x8(qsrc + kk * 32) : zero_f16x8();
+    for (int c = tid; c < NW * 16 * (DR / 8); c += NT) {
+        const int r = c / (DR / 8), col = c - r * (DR / 8);
+        const int qrow = z * (NW * 16) + r;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (qrow < RQ) v = *reinterpret_cast<const u32x4*>(qhat + ((size_t)b * RQ + qrow) * W + RK + col * 8);
+        *reinterpret_cast<u32x4*>(qr_lds + r * QRS + col * 8) = v;
+    }
+    const u16* qr_row = qr_lds + (wave * 16 + r16) * QRS + q4 * 8;
 
     floatx4 uacc[NU];
 #pragma unroll
     for (int n = 0; n < NU; ++n) uacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
     SoftmaxState st{kNegInf, 0.f};
 
-    for (int it = 0; it < ntiles; ++it) {
+    // barrier without the compiler's memory fence (whose vmcnt(0) would drain the
+    // direct loads still in flight): own LDS operations complete, then s_barrier
+    auto block_sync = [&]() {
+        asm volatile("" ::: "memory");
+        // s_waitcnt lgkmcnt(0): vmcnt field at its maximum 63 (bits [3:0] and [15:14]),
+        // expcnt at 7, lgkmcnt (bits [11:8]) at 0
+        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // convert this lane's own DMA slots of tile `it` (in the buffer at `lds`) to fp16 in
+    // place once its loads have landed; slots of rows past the chunk, pads and spare
+    // slots become zero.  No other lane touches these slots, so no barrier is needed
+    // before it, and the barrier at the top of the next iteration publishes the result.
+    auto convert_own = [&](int it, u16* lds) {
+        const int lim = min(TT, t1 - t0 - it * TT) * W * 2;
+        u32x4 v[NDMA];
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) v[i] = *reinterpret_cast<const u32x4*>(lds + ((i * NW + wave) * 64 + lane) * 8);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const bool keep = dma_off[i] >= 0 && dma_off[i] < lim;
+            *reinterpret_cast<u32x4*>(lds + ((i * NW + wave) * 64 + lane) * 8) =
+                keep ? bf8_to_h8(v[i]) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    // one tile: (barrier) start the loads of tile it+2, compute tile it, then wait for
+    // this wave's loads of tile it+1 and convert them.  One barrier per tile: it marks
+    // tile it converted by every wave and tile it-1 (whose buffer the new loads reuse)
+    // consumed by every wave.
+    auto step = [&](int it, u16* lds, uint32_t dma_buf, u16* next_lds) {
         const int tb = t0 + it * TT;
-        __syncthreads();
-        if (!active) continue;
-        const u16* lds = buf + (it & 1) * TILE;
-
-        float sc[8];
-        {
-            // two independent accumulator chains per 16-token half; the operands of
-            // k-step kk+1 are read from LDS before the MFMAs of k-step kk are issued
-            floatx4 acc[2][2] = {};
-            const u16* arow = lds + r16 * STRIDE + q4 * 8;
-            f16x8 a0 = ld_f16x8(arow), a1 = ld_f16x8(arow + 16 * STRIDE), bq = ld_f16x8(qrow_lds);
+        block_sync();
+        if (it + 2 < ntiles) dma_tile(it + 2, dma_buf);
+        if (active) {
+            float sc[8];
+            {
+                floatx4 acc[2] = {};
+                const u16* arow = lds + r16 * STRIDE + q4 * 8;
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                f16x8 n0 = a0, n1 = a1, nb = bq;
-                if (kk + 1 < KS) {
-                    n0 = ld_f16x8(arow + (kk + 1) * 32);
-                    n1 = ld_f16x8(arow + 16 * STRIDE + (kk + 1) * 32);
-                    nb = ld_f16x8(qrow_lds + (kk + 1) * 32);
+                for (int kk = 0; kk < KS; ++kk) {
+                    const f16x8 bq = kk < KL ? qv[kk] : ld_f16x8(qr_row + (kk - KL) * 32);
+                    acc[0] = mfma16h(ld_f16x8(arow + kk * 32), bq, acc[0]);
+                    acc[1] = mfma16h(ld_f16x8(arow + 16 * STRIDE + kk * 32), bq, acc[1]);
+                    // bound how far the scheduler hoists operand reads (register pressure)
+                    if (kk % 6 == 5) __builtin_amdgcn_sched_barrier(0);
                 }
-                acc[0][kk & 1] = mfma16h(a0, bq, acc[0][kk & 1]);
-                acc[1][kk & 1] = mfma16h(a1, bq, acc[1][kk & 1]);
-                a0 = n0;
-                a1 = n1;
-                bq = nb;
-            }
 #pragma unroll
-            for (int th = 0; th < 2; ++th) {
+                for (int th = 0; th < 2; ++th) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = tb + th * 16 + q4 * 4 + i;
-                    const float v = acc[th][0][i] + acc[th][1][i];
-                    sc[th * 4 + i] = (row_ok && t < t1 && t < nvis) ? v * scale_log2 : kNegInf;
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = tb + th * 16 + q4 * 4 + i;
+                        sc[th * 4 + i] = (row_ok && t < t1 && t < nvis) ? acc[th][i] * scale_log2 : kNegInf;
+                    }
                 }
             }
-        }
-        bool rescale;
-        float alpha;
-        const f16x8 pb = softmax_tile(st, sc, rescale, alpha);
-        if (__builtin_expect(rescale, 0)) {
-            // rare (the reference rose by more than kLazy); kept as a real branch so the
-            // accumulators are not touched by VALU on the common path
-            asm volatile("" ::: "memory");
+            bool rescale;
+            float alpha;
+            const f16x8 pb = softmax_tile(st, sc, rescale, alpha);
+            if (__builtin_expect(rescale, 0)) {
+                // rare (the reference rose by more than kLazy); kept as a real branch so the
+                // accumulators are not touched by VALU on the common path
+                asm volatile("" ::: "memory");
 #pragma unroll
-            for (int n = 0; n < NU; ++n) uacc[n] *= alpha;
-        }
-        {
-            // PV with the A operand of column tile n+2 read ahead of MFMA n
-            f16x8 c0 = gather_col(lds, STRIDE, q4, r16, 0), c1 = gather_col(lds, STRIDE, q4, r16, 16);
+                for (int n = 0; n < NU; ++n) uacc[n] *= alpha;
+            }
 #pragma unroll
             for (int n = 0; n < NU; ++n) {
-                f16x8 c2 = c0;
-                if (n + 2 < NU) c2 = gather_col(lds, STRIDE, q4, r16, 16 * (n + 2));
-                uacc[n] = mfma16h(c0, pb, uacc[n]);
-                c0 = c1;
-                c1 = c2;
+                uacc[n] = mfma16h(gather_col(lds, STRIDE, q4, r16, 16 * n), pb, uacc[n]);
+                if (n % 8 == 7) __builtin_amdgcn_sched_barrier(0);
             }
         }
+        if (it + 1 < ntiles) {
+            if (it + 2 < ntiles) wait_vmcnt<NDMA>();    // tile it+2's loads may stay in flight
+            else wait_vmcnt<0>();
+            convert_own(it + 1, next_lds);
+        }
+    };
+
+    const uint32_t a0 = lds_addr(buf0), a1 = lds_addr(buf1), a2 = lds_addr(buf2);
+    dma_tile(0, a0);
+    if (ntiles > 1) dma_tile(1, a1);
+    if (ntiles > 1) wait_vmcnt<NDMA>();
+    else wait_vmcnt<0>();
+    convert_own(0, buf0);
+    for (int it = 0; it < ntiles; it += NBUF) {
+        step(it, buf0, a2, buf1);
+        if (it + 1 < ntiles) step(it + 1, buf1, a0, buf2);
+        if (it + 2 < ntiles) step(it + 2, buf2, a1, buf0);
     }
     if (!active) return;
 
@@ -569,7 +637,7 @@ hipError_t launch_gqa_g(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int absorb_waves(int query_rows) { return query_rows <= 32 ? 2 : 4; }
+int absorb_waves(int query_rows) { return query_rows <= 32 ? 2 : (query_rows <= 64 ? 4 : 8); }
 
 bool gqa_bf16_supported(int g, int rows_per_group) {
     return (g == 1 || g == 2 || g == 4 || g == 8) && rows_per_group >= 1;
@@ -601,17 +669,18 @@ hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st) {
     dim3 grid(((pairs + 7) / 8) * 8 * nz);
     e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;
+#define GQLA_ABSORB_LAUNCH(NWV)                                                                          \
+    hipLaunchKernelGGL(absorb_decode_kernel<NWV>, grid, dim3(NWV * 64), 0, st, (const u16*)a.qhat,             \
+                       (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens, a.max_ctx, a.h_q, a.g,   \
+                       a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e, a.part_o, a.part_lse)
     if (nw == 2) {
-        hipLaunchKernelGGL(absorb_decode_kernel<2>, grid, dim3(6 * 64), 0, st,
-                           (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
-                           a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e,
-                           a.part_o, a.part_lse);
+        GQLA_ABSORB_LAUNCH(2);
+    } else if (nw == 4) {
+        GQLA_ABSORB_LAUNCH(4);
     } else {
-        hipLaunchKernelGGL(absorb_decode_kernel<4>, grid, dim3(8 * 64), 0, st,
-                           (const u16*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens,
-                           a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e,
-                           a.part_o, a.part_lse);
+        GQLA_ABSORB_LAUNCH(8);
     }
+#undef GQLA_ABSORB_LAUNCH
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return record_if(a.ev_after, st);
