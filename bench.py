@@ -219,12 +219,13 @@ def main(argv=None):
                 "n_split": splits[0], "chunk": splits[1]}
 
     rq = cfg.s_q * cfg.h_q
-    absorb_name = "absorb_decode_kernel<%d>" % (2 if rq <= 32 else (4 if rq <= 64 else 8))
+    absorb_name = "absorb_decode_kernel<%d, 1>" % (2 if rq <= 32 else (4 if rq <= 64 else 8))
     paths = {"absorb": path_rec(work_a, call_a, kern_a, split_a, absorb_name),
              "gqa": path_rec(work_g, call_g, kern_g, split_g, "gqa_decode_kernel<8, 8>")}
 
     # dominant kernel: the longer of the two main attention kernels
-    kernel_src = ["latent_kv_cache_amd/csrc/decode_bf16.hip", "latent_kv_cache_amd/csrc/common.h"]
+    kernel_src = ["latent_kv_cache_amd/csrc/decode_gqa.hip", "latent_kv_cache_amd/csrc/decode_absorb.hip",
+                  "latent_kv_cache_amd/csrc/common.h"]
     digest = sources_digest(kernel_src)
     if kern_g >= kern_a:
         # bytes per launch: expanded rows of every cached token, queries in, outputs out

@@ -24,17 +24,22 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgqla.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "decode_bf16.hip", "expand_bf16.hip", "f32_path.hip", "combine.hip"]
+SOURCES = ["api.hip", "decode_gqa.hip", "decode_absorb.hip", "expand_bf16.hip", "f32_path.hip", "combine.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
-    # MFMA accumulators in ordinary VGPRs: the decode loops rescale them with VALU,
-    # and accumulators in AGPRs would be copied to VGPRs and back every tile
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+
+# Per-source extras.  The decode kernels keep their MFMA accumulators in ordinary
+# VGPRs: they rescale them with VALU, and AGPR accumulators would be copied to VGPRs
+# and back every tile.
+EXTRA_FLAGS = {
+    "decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode_absorb.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc() -> str:
@@ -46,7 +51,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

@@ -91,7 +91,7 @@ Plan plan(const gqla_shape& s, int path, int batch, int max_ctx, int num_splits)
     } else {
         int units = batch > 0 ? batch : 1;
         if (s.dtype == GQLA_BF16 && path == GQLA_PATH_ABSORB) {
-            const int rows = 16 * gqla::absorb_waves(s.s_q * s.h_q);
+            const int rows = gqla::absorb_block_rows(s.s_q * s.h_q);
             units *= (s.s_q * s.h_q + rows - 1) / rows;
         }
         const int cus = device_cus();

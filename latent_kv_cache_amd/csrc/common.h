@@ -72,7 +72,13 @@ __device__ __forceinline__ u32x4 bf8_to_h8(u32x4 v) {
 // fp32 -> fp16, round to nearest even.
 __device__ __forceinline__ u16 f2h(float f) { return __builtin_bit_cast(u16, (_Float16)f); }
 
-__device__ __forceinline__ uint32_t pack2h(float lo, float hi) { return pack2(f2h(lo), f2h(hi)); }
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two packed fp16, round to nearest even (one v_cvt_pk_f16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2{lo, hi}), halfx2));
+}
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -89,17 +95,28 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const u16* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over the four lanes l%16 + 16q (q = 0..3) that hold one matrix row, with
+// gfx950's cross-row VALU permutes instead of LDS-routed shuffles.  permlane16_swap
+// exchanges the odd 16-lane rows of its first operand with the even rows of its second;
+// permlane32_swap exchanges the upper half of the first with the lower half of the
+// second.  Called with the same value twice, the two results hold, in every lane, the
+// values of lanes l and l^16 (then l and l^32), one in each result.
 __device__ __forceinline__ float wave_max16x4(float v) {
-    // max over the four lanes l%16 + 16*q (q = 0..3) that hold one matrix row
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    const uint32_t x = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t y = __float_as_uint(v);
+    const auto c = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
 __device__ __forceinline__ float wave_sum16x4(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    const uint32_t x = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t y = __float_as_uint(v);
+    const auto c = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }

@@ -1,0 +1,295 @@
+// bf16 MFMA GQA decode kernel for gfx950.
+//
+// Method: "GQLA: Group-Query Latent Attention for Hardware-Adaptive LLM
+// Decoding", technical summary section 2 (Architecture, GQA path).  Per sequence b,
+// query token s and head i of group j = i / (h_q/g), softmax attention over the
+// visible cached tokens t <= L_b - s_q + s of the once-expanded group rows:
+//   score_t = scale [q^N | q^R].[K_j,t | k_R,t],  o = sum_t p_t V_j,t
+// over one context chunk per workgroup (split-K).  Each workgroup writes the chunk's
+// normalised output and its log-sum-exp; launch_combine merges them.
+//
+// Tiling.  A workgroup streams its chunk in tiles of 32 cache rows.  A tile is
+// one contiguous span of HBM (rows of a sequence are packed), loaded with
+// 16-byte vector loads into registers one tile ahead and stored into LDS with
+// a 32-byte pad per row.  On gfx950 a row stride of 8 x (odd) dwords modulo the 64
+// LDS banks lets the 16-byte operand reads of 16 rows, and the transposing reads of
+// 4 rows x 32 bytes, proceed at close to the full LDS rate (a 16-byte pad, 36 dwords
+// mod 64, measured at about 60 % of it).
+// HBM holds bf16; the tile is converted to fp16 on its way into LDS (exact for
+// bf16 values within fp16's range) and the contractions run on fp16 MFMA, so the
+// softmax weights P, which the kernel itself rounds, keep 10 mantissa bits instead
+// of 7.
+// Each wave owns 16 query rows (the N = 16 side of the 16x16x32 MFMA: the 16 heads
+// of a group at h_q/g = 16) and keeps its queries and accumulators in registers:
+//   S^T[token][row] = K_tile . Q^T   (A = cache rows from LDS, B = queries)
+//   O^T[feat][row] += V_tile^T . P^T (A = cache columns from LDS, B = P)
+// so the softmax state of a row lives in the four lanes l%16 + 16q.
+#include "common.h"
+#include "launch.h"
+
+namespace gqla {
+
+namespace {
+
+constexpr int DH = 128;   // per-group key/value width
+constexpr int DR = 64;    // rotary key width
+constexpr int RK = 512;   // latent width
+constexpr int TT = 32;    // tokens per tile
+
+// Token held by k-slot e (0..7) of lane group q (0..3) in the P / V^T operands:
+// the softmax keeps S for tokens 16*(e/4) + 4q + (e%4), the D-layout of the two
+// 16-token halves of S^T.
+__device__ __forceinline__ int slot_token(int q, int e) { return 16 * (e >> 2) + 4 * q + (e & 3); }
+
+// Online softmax with a lazily raised reference.  Exponentials are taken against a
+// per-row reference m (log2 domain) that is raised only when a tile's maximum exceeds
+// it by more than kLazy; otherwise p = 2^(s - m) <= 2^kLazy, which fp16 P and fp32
+// sums hold as precisely as values <= 1.  When no row of the wave raises its
+// reference, the accumulators need no rescaling for that tile.  The final
+// normalisation and log-sum-exp use the same reference, so the result is that of
+// the exact softmax.
+constexpr float kLazy = 10.f;
+
+struct SoftmaxState {
+    float m;   // reference (log2 domain), identical in the 4 lanes of a row; -inf before any row
+    float l;   // lane-partial running sum of 2^(s - m)
+};
+
+// sc[e] are log2-scaled scores for slot_token(q4, e), masked slots -inf.  Returns P as
+// the fp16 B operand; sets rescale (wave-uniform) and alpha when accumulators must be
+// multiplied by alpha before this tile's P is added.
+__device__ __forceinline__ f16x8 softmax_tile(SoftmaxState& st, float (&sc)[8], bool& rescale, float& alpha) {
+    float mt = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
+    mt = wave_max16x4(mt);
+    const bool raise = mt > st.m + kLazy;        // false while the row has seen nothing
+    rescale = __any(raise);
+    alpha = 1.f;
+    if (raise) {
+        alpha = fast_exp2(st.m - mt);            // st.m = -inf gives 0
+        st.l *= alpha;
+        st.m = mt;
+    }
+    const float muse = (st.m == kNegInf) ? 0.f : st.m;
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(sc[e] - muse);
+        ps += p[e];
+    }
+    st.l += ps;
+    u32x4 pk;
+    pk[0] = pack2h(p[0], p[1]);
+    pk[1] = pack2h(p[2], p[3]);
+    pk[2] = pack2h(p[4], p[5]);
+    pk[3] = pack2h(p[6], p[7]);
+    return as_f16x8(pk);
+}
+
+// A operand of O^T += V^T P^T: lane (q4, r16) needs column col0 + r16 of the tile at
+// the eight slot tokens 4q4 + e and 16 + 4q4 + e (e = 0..3).  Lane m of the 16-lane
+// group addresses row 4q4 + m/4 (then 16 rows further), columns col0 + 4(m%4)..+3;
+// the transposing read hands lane j column col0 + j of those rows.
+__device__ __forceinline__ f16x8 gather_col(const u16* lds, int stride, int q4, int r16, int col0) {
+    const u16* p0 = lds + (4 * q4 + (r16 >> 2)) * stride + col0 + 4 * (r16 & 3);
+    const u32x2 lo = lds_read_tr16(p0);
+    const u32x2 hi = lds_read_tr16(p0 + 16 * stride);
+    return as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Copy rows [row0, row0 + nrows) of a packed row-major span (width W elements) into
+// registers: chunk c = tid + k*NT of the tile, 16 bytes each.  Rows past nrows load zeros.
+template <int W, int NT, int NLOAD>
+__device__ __forceinline__ void load_tile(u32x4 (&reg)[NLOAD], const u16* __restrict__ base, int nrows, int tid) {
+    constexpr int CPR = W / 8;   // 16-byte chunks per row
+#pragma unroll
+    for (int k = 0; k < NLOAD; ++k) {
+        const int c = tid + k * NT;
+        const int r = c / CPR;
+        if (c < TT * CPR && r < nrows) {
+            reg[k] = *reinterpret_cast<const u32x4*>(base + (size_t)c * 8);
+        } else {
+            reg[k] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+// Store the staged tile into LDS as fp16 (bf16 -> fp16 conversion per element).
+template <int W, int STRIDE, int NT, int NLOAD>
+__device__ __forceinline__ void store_tile(u16* lds, const u32x4 (&reg)[NLOAD], int tid) {
+    constexpr int CPR = W / 8;
+#pragma unroll
+    for (int k = 0; k < NLOAD; ++k) {
+        const int c = tid + k * NT;
+        if (c < TT * CPR) {
+            const int r = c / CPR;
+            const int col = c - r * CPR;
+            *reinterpret_cast<u32x4*>(lds + r * STRIDE + col * 8) = bf8_to_h8(reg[k]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// GQA decode.  grid = (n_split, batch, pair blocks); block = NW waves.  The
+// (group, 16-row tile) pairs of a sequence are numbered pair = j*RT + rt with
+// RT = ceil(rows_per_group / 16); block z handles pairs [z*NW, z*NW + NW).
+// Rows of group j are numbered rho = s*hpg + hh (query token s, head j*hpg + hh).
+// ---------------------------------------------------------------------------
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
+    const u16* __restrict__ q_nope, const u16* __restrict__ q_rope,
+    const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
+    int max_ctx, int h_q, int s_q, int chunk, int batch, float scale_log2,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    constexpr int W = 2 * G * DH + DR;
+    constexpr int STRIDE = W + 16;   // row stride = 8 x odd dwords mod 64 banks
+    constexpr int NT = NW * 64;
+    constexpr int NLOAD = (TT * (W / 8) + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) u16 lds[TT * STRIDE];
+
+    const int p = blockIdx.x, b = blockIdx.y;
+    const int L = clampi(ctx_lens[b], 0, max_ctx);
+    const int t0 = p * chunk;
+    if (t0 >= L) return;                      // uniform over the block
+    const int t1 = min(t0 + chunk, L);
+    const int ntiles = (t1 - t0 + TT - 1) / TT;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int q4 = lane >> 4, r16 = lane & 15;
+    const int hpg = h_q / G;
+    const int rows_g = s_q * hpg;
+    const int RT = (rows_g + 15) >> 4;
+    const int pair = blockIdx.z * NW + wave;
+    const bool active = pair < G * RT;
+    const int j = active ? pair / RT : 0;
+    const int rt = active ? pair - j * RT : 0;
+    const int rho = rt * 16 + r16;
+    const bool row_ok = active && rho < rows_g;
+    const int s = row_ok ? rho / hpg : 0;
+    const int h = j * hpg + (row_ok ? rho - s * hpg : 0);
+    const int nvis = clampi(L - s_q + s + 1, 0, L);
+    const int qrow = (b * s_q + s) * h_q + h;
+
+    // queries as the B operand of S^T = K Q^T: k-steps 0..3 over q^N, 4..5 over q^R
+    f16x8 qv[6];
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) {
+        if (row_ok) {
+            const u16* src = kk < 4 ? q_nope + (size_t)qrow * DH + kk * 32 + q4 * 8
+                                    : q_rope + (size_t)qrow * DR + (kk - 4) * 32 + q4 * 8;
+            qv[kk] = as_f16x8(bf8_to_h8(*reinterpret_cast<const u32x4*>(src)));
+        } else {
+            qv[kk] = zero_f16x8();
+        }
+    }
+
+    floatx4 oacc[DH / 16];
+#pragma unroll
+    for (int n = 0; n < DH / 16; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    SoftmaxState st{kNegInf, 0.f};
+
+    const u16* seq = cache + (size_t)b * bstride;
+    u32x4 reg[NLOAD];
+    load_tile<W, NT, NLOAD>(reg, seq + (size_t)t0 * W, min(TT, t1 - t0), tid);
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int tb = t0 + it * TT;
+        if (it > 0) __syncthreads();
+        store_tile<W, STRIDE, NT, NLOAD>(lds, reg, tid);
+        __syncthreads();
+        if (it + 1 < ntiles) {
+            const int tn = tb + TT;
+            load_tile<W, NT, NLOAD>(reg, seq + (size_t)tn * W, min(TT, t1 - tn), tid);
+        }
+        if (!active) continue;
+
+        float sc[8];
+        {
+            // two independent accumulator chains per 16-token half
+            floatx4 acc[2][2] = {};
+#pragma unroll
+            for (int kk = 0; kk < 6; ++kk) {
+                const int col = kk < 4 ? j * DH + kk * 32 + q4 * 8 : 2 * G * DH + (kk - 4) * 32 + q4 * 8;
+#pragma unroll
+                for (int th = 0; th < 2; ++th)
+                    acc[th][kk & 1] = mfma16h(ld_f16x8(lds + (th * 16 + r16) * STRIDE + col), qv[kk], acc[th][kk & 1]);
+            }
+#pragma unroll
+            for (int th = 0; th < 2; ++th) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tb + th * 16 + q4 * 4 + i;
+                    const float v = acc[th][0][i] + acc[th][1][i];
+                    sc[th * 4 + i] = (row_ok && t < t1 && t < nvis) ? v * scale_log2 : kNegInf;
+                }
+            }
+        }
+        bool rescale;
+        float alpha;
+        const f16x8 pb = softmax_tile(st, sc, rescale, alpha);
+        if (__builtin_expect(rescale, 0)) {
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int n = 0; n < DH / 16; ++n) oacc[n] *= alpha;
+        }
+        const int vcol = (G + j) * DH;
+#pragma unroll
+        for (int n = 0; n < DH / 16; ++n)
+            oacc[n] = mfma16h(gather_col(lds, STRIDE, q4, r16, vcol + 16 * n), pb, oacc[n]);
+    }
+    if (!row_ok) return;
+
+    const float l = wave_sum16x4(st.l);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
+    float* po = part_o + prow * DH;
+#pragma unroll
+    for (int n = 0; n < DH / 16; ++n) {
+        *reinterpret_cast<floatx4*>(po + 16 * n + 4 * q4) = oacc[n] * inv;
+    }
+    if (q4 == 0) part_lse[prow] = l > 0.f ? (st.m + __log2f(l)) * kLn2 : kNegInf;
+}
+
+template <int G, int NW>
+hipError_t launch_gqa_t(const DecodeArgs& a, hipStream_t st) {
+    const int rows_g = a.s_q * (a.h_q / a.g);
+    const int pairs = G * ((rows_g + 15) / 16);
+    dim3 grid(a.n_split, a.batch, (pairs + NW - 1) / NW);
+    hipError_t e = record_if(a.ev_before, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gqa_decode_kernel<G, NW>), grid, dim3(NW * 64), 0, st,
+                       (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.cache, a.bstride,
+                       a.ctx_lens, a.max_ctx, a.h_q, a.s_q, a.chunk, a.batch, a.scale * kLog2e,
+                       a.part_o, a.part_lse);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return record_if(a.ev_after, st);
+}
+
+// 8 waves per block: with 1024-thread blocks the 128-register cap spills the
+// staging registers; extra (group, row tile) pairs go to further blocks in z.
+template <int G>
+hipError_t launch_gqa_g(const DecodeArgs& a, hipStream_t st) {
+    return launch_gqa_t<G, 8>(a, st);
+}
+
+}  // namespace
+
+bool gqa_bf16_supported(int g, int rows_per_group) {
+    return (g == 1 || g == 2 || g == 4 || g == 8) && rows_per_group >= 1;
+}
+
+hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t st) {
+    switch (a.g) {
+        case 1: return launch_gqa_g<1>(a, st);
+        case 2: return launch_gqa_g<2>(a, st);
+        case 4: return launch_gqa_g<4>(a, st);
+        case 8: return launch_gqa_g<8>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gqla

@@ -47,7 +47,7 @@ hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_expand_bf16(const ExpandArgs& a, hipStream_t st);
 bool gqa_bf16_supported(int g, int rows_per_group);
-int absorb_waves(int query_rows);          // waves (16 query rows each) per absorb workgroup
+int absorb_block_rows(int query_rows);     // query rows per absorb workgroup (32, 64 or 128)
 
 // fp32 vector path (generic dims within the documented bounds)
 hipError_t launch_absorb_f32(const DecodeArgs& a, hipStream_t st);

@@ -123,6 +123,46 @@ def test_chunk_boundary_causal(gqla):
     both_paths(cfg, [97, 65], gqla, 2, max_ctx=129, what="causal-boundary")
 
 
+def test_rising_scores(gqla):
+    """Latent rows whose scale grows along the sequence, so the softmax maximum rises by
+    more than the online softmax's slack (10 log2 units) after rows have accumulated:
+    the kernels must raise their reference and rescale what they hold (a ramp on
+    sequence 0, a sudden jump on sequence 1; a replay of the lazy-reference rule on the
+    CPU counts 24 and 57 such raises over the heads).  The peak logits stay near 10:
+    the absorb path rounds its absorbed query to fp16, an error that grows with |score|,
+    and far sharper softmaxes amplify it past the tolerance."""
+    import oracle
+    torch = gu.torch_mod()
+    cfg = synth.config(3).with_(batch=2)
+    lens = [1000, 700]
+    w = gu.workload(cfg, lens=lens)
+    qn, qr = synth.queries(cfg)
+    w_uk, w_uv = synth.up_weights(cfg)
+    rows = {}
+    for b, L in enumerate(lens):
+        t = np.arange(L, dtype=np.float64)
+        if b == 0:
+            f = np.where(t < 300, 0.1, 0.1 + 2.5 * (t - 300) / (L - 300))
+        else:
+            f = np.where(t < 400, 0.15, 2.4)
+        rows[b] = synth.bf16_round(synth.latent_rows(cfg, b, L).astype(np.float64) * f[:, None])
+        w.latent[b, :L].copy_(torch.from_numpy(rows[b]).to(w.dtype))
+    note("rising scores absorb")
+    out, lse = gu.run_absorb(w, gqla, 1)
+    gu.compare(cfg, out, lse, [0, 1], w.lens, "rising absorb",
+               ref=lambda b, L: oracle.textbook_decode(rows[b], qn[b], qr[b], w_uk, w_uv, L, cfg.scale))
+    note("rising scores gqa over stored rows")
+    width = 2 * cfg.g * cfg.d_h + cfg.d_r
+    gc = torch.zeros((2, w.max_ctx, width), dtype=w.dtype, device="cuda")
+    stored = {}
+    for b, L in enumerate(lens):
+        stored[b] = synth.bf16_round(oracle.expand_groups(rows[b], w_uk, w_uv))
+        gc[b, :L].copy_(torch.from_numpy(stored[b]).to(w.dtype))
+    out2, lse2 = gu.run_gqa(w, gqla, gc, 1)
+    gu.compare(cfg, out2, lse2, [0, 1], w.lens, "rising gqa",
+               ref=lambda b, L: oracle.gqa_decode(stored[b], qn[b], qr[b], cfg.g, L, cfg.scale))
+
+
 # ---------------------------------------------------------------- properties
 def test_split_invariance_and_determinism(gqla):
     cfg = synth.config(3).with_(batch=2)
