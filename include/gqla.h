@@ -126,6 +126,69 @@ gqla_status gqla_decode_gqa(const gqla_shape* shape, int32_t batch, int32_t max_
                             void* workspace, size_t workspace_bytes,
                             int32_t num_splits, void* stream);
 
+/* Decode-step append (the step that feeds both decode paths; section 2,
+ * Architecture: one latent row and one shared rotary key per token, a rotary query
+ * part per head).  For every sequence b and new token s < s_q, at position
+ * t = L_b - s_q + s (L_b = ctx_lens[b] clamped to [0, max_ctx], the new tokens
+ * included; tokens with t < 0 are skipped):
+ *   latent[b][t]        = [c_new[b][s] | RoPE_t(kr_new[b][s])]
+ *   q_rope_out[b][s][h] = RoPE_t(q_rope_raw[b][s][h])          (when q_rope_raw != NULL)
+ *   group_cache[b][t]   = the expansion of latent[b][t] as in gqla_expand_groups
+ *                                                                (when group_cache != NULL)
+ * RoPE pairs component k < d_r/2 with k + d_r/2 and turns the pair by the angle
+ * t * rope_theta^(-2k/d_r) (x' = x cos - y sin, y' = x sin + y cos).  Angles and
+ * rotated values are computed in fp64 and rounded once to fp32, then for bf16 to bf16
+ * (round to nearest even); the expansion accumulates in fp32 (RNE to the dtype).
+ *   c_new       [batch][s_q][r_kv]        new latent rows
+ *   kr_new      [batch][s_q][d_r]         new rotary keys before rotation
+ *   q_rope_raw  [batch][s_q][h_q][d_r]    rotary query parts before rotation, or NULL
+ *   q_rope_out  same shape; NULL exactly when q_rope_raw is NULL (may not alias it)
+ *   latent, latent_bstride                as in gqla_expand_groups (rows written)
+ *   w_uk, w_uv  [g][d_h][r_kv], required when group_cache is not NULL
+ *   rope_theta  rotary base, finite and > 0 (10000 in the workloads); d_r must be even.
+ * Only the rows and entries listed are written. */
+gqla_status gqla_append_rows(const gqla_shape* shape, int32_t batch, int32_t max_ctx,
+                             const void* c_new, const void* kr_new,
+                             const void* q_rope_raw, void* q_rope_out, float rope_theta,
+                             const int32_t* ctx_lens,
+                             void* latent, int64_t latent_bstride,
+                             const void* w_uk, const void* w_uv,
+                             void* group_cache, int64_t group_bstride, void* stream);
+
+/* Roofline path selection (section 2, Path selection: the runtime picks the decode
+ * path per device without retraining; section 1 gives the two devices' ridges).
+ * For path in {absorb, GQA} and s_q in 1..shape->s_q (the most query tokens the model
+ * proposes per step), a decode step over contexts summing to total_ctx takes
+ * max(bytes / peak_bytes_per_s, flops / peak_flops) with, per cached token,
+ *   absorb: bytes e (r_kv + d_r),     flops 2 s_q h_q (2 r_kv + d_r)
+ *   GQA:    bytes e (2 g d_h + d_r),  flops 2 s_q h_q (2 d_h + d_r)
+ * (e = 2 for bf16, 4 for fp32) and yields batch * s_q query tokens.  The choice is the
+ * configuration with the most query tokens per second; on a tie the smaller s_q, then
+ * the absorb path.  Host-only arithmetic: any device's peaks may be given (for this
+ * one, gqla_measure_peaks measures them).  g is a property of the weights and is taken
+ * from the shape. */
+typedef struct gqla_path_choice {
+    int32_t path;               /* gqla_path */
+    int32_t s_q;                /* query tokens per step */
+    int32_t compute_bound;      /* 1: the flops term sets the step time */
+    int32_t reserved;           /* 0 */
+    double tokens_per_s;        /* roofline query tokens per second */
+} gqla_path_choice;
+
+gqla_status gqla_select_path(const gqla_shape* shape, int32_t batch, int64_t total_ctx,
+                             double peak_flops, double peak_bytes_per_s,
+                             gqla_path_choice* choice);
+
+/* Measure this device's achievable HBM read bandwidth (one streaming pass over the
+ * scratch buffer, best of three after a warm-up pass) and dense bf16 MFMA rate (four
+ * independent 16x16x32 chains per wave, 32 waves per compute unit), for
+ * gqla_select_path.  scratch: device buffer of at least 64 MiB, 16-byte aligned, owned
+ * by the caller; its contents are overwritten.  A buffer well above the last-level
+ * cache (1 GiB or more on MI355X) measures HBM rather than cache.  Unlike the other
+ * calls this one waits for its kernels: it returns when both measurements are done. */
+gqla_status gqla_measure_peaks(void* scratch, size_t scratch_bytes, double* bytes_per_s,
+                               double* flops_per_s, void* stream);
+
 /* Timing hook for measurement tools.  When both are non-NULL, every later decode
  * call on this thread records `before` (a hipEvent_t) on its stream right before
  * launching its main attention kernel and `after` right after it, so that

@@ -3,6 +3,7 @@
 // contract of each entry point are in include/gqla.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -301,6 +302,112 @@ gqla_status gqla_decode_gqa(const gqla_shape* shape, int32_t batch, int32_t max_
                             int32_t num_splits, void* stream) {
     return decode_common(GQLA_PATH_GQA, shape, batch, max_ctx, q_nope, q_rope, nullptr, nullptr, group_cache,
                          group_bstride, ctx_lens, out, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+gqla_status gqla_append_rows(const gqla_shape* shape, int32_t batch, int32_t max_ctx, const void* c_new,
+                             const void* kr_new, const void* q_rope_raw, void* q_rope_out, float rope_theta,
+                             const int32_t* ctx_lens, void* latent, int64_t latent_bstride, const void* w_uk,
+                             const void* w_uv, void* group_cache, int64_t group_bstride, void* stream) {
+    // the group layout checks of the GQA path apply when new rows are expanded
+    TRY(check_shape(shape, group_cache ? GQLA_PATH_GQA : GQLA_PATH_ABSORB));
+    TRY(check_sizes(batch, max_ctx));
+    const gqla_shape& s = *shape;
+    if (s.d_r % 2) return fail(GQLA_ERR_INVALID_ARG, "d_r=%d is odd", s.d_r);
+    if (s.d_r > 256) return fail(GQLA_ERR_UNSUPPORTED, "d_r=%d > 256", s.d_r);
+    if (!(rope_theta > 0.f) || !std::isfinite(rope_theta))
+        return fail(GQLA_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+    if ((q_rope_raw == nullptr) != (q_rope_out == nullptr))
+        return fail(GQLA_ERR_INVALID_ARG, "q_rope_raw and q_rope_out must both be set or both be null");
+    if (batch == 0 || max_ctx == 0) return ok();
+    TRY(check_ptr(c_new, "c_new"));
+    TRY(check_ptr(kr_new, "kr_new"));
+    if (q_rope_raw) {
+        TRY(check_ptr(q_rope_raw, "q_rope_raw"));
+        TRY(check_ptr(q_rope_out, "q_rope_out"));
+        if (q_rope_raw == q_rope_out) return fail(GQLA_ERR_INVALID_ARG, "q_rope_out aliases q_rope_raw");
+    }
+    if (!ctx_lens) return fail(GQLA_ERR_INVALID_ARG, "ctx_lens is null");
+    TRY(check_ptr(latent, "latent"));
+    TRY(check_stride(latent_bstride, s.r_kv + s.d_r, max_ctx, "latent_bstride"));
+    if (group_cache) {
+        TRY(check_ptr(w_uk, "w_uk"));
+        TRY(check_ptr(w_uv, "w_uv"));
+        TRY(check_ptr(group_cache, "group_cache"));
+        TRY(check_stride(group_bstride, 2LL * s.g * s.d_h + s.d_r, max_ctx, "group_bstride"));
+    }
+    gqla::AppendArgs a;
+    a.h_q = s.h_q;
+    a.g = s.g;
+    a.r_kv = s.r_kv;
+    a.d_r = s.d_r;
+    a.d_h = s.d_h;
+    a.s_q = s.s_q;
+    a.batch = batch;
+    a.max_ctx = max_ctx;
+    a.theta = rope_theta;
+    a.c_new = c_new;
+    a.kr_new = kr_new;
+    a.q_rope_raw = q_rope_raw;
+    a.q_rope_out = q_rope_out;
+    a.ctx_lens = ctx_lens;
+    a.latent = latent;
+    a.latent_bstride = latent_bstride;
+    a.w_uk = w_uk;
+    a.w_uv = w_uv;
+    a.group_cache = group_cache;
+    a.group_bstride = group_bstride;
+    return hip_status(gqla::launch_append(a, s.dtype == GQLA_BF16, static_cast<hipStream_t>(stream)), "append launch");
+}
+
+gqla_status gqla_select_path(const gqla_shape* shape, int32_t batch, int64_t total_ctx, double peak_flops,
+                             double peak_bytes_per_s, gqla_path_choice* choice) {
+    if (!shape) return fail(GQLA_ERR_INVALID_ARG, "shape is null");
+    const gqla_shape& s = *shape;
+    if (s.h_q <= 0 || s.g <= 0 || s.r_kv <= 0 || s.d_r <= 0 || s.d_h <= 0)
+        return fail(GQLA_ERR_INVALID_ARG, "dims must be positive");
+    if (s.h_q % s.g != 0) return fail(GQLA_ERR_INVALID_ARG, "h_q=%d is not a multiple of g=%d", s.h_q, s.g);
+    if (s.s_q < 1 || s.s_q > 4) return fail(GQLA_ERR_INVALID_ARG, "s_q=%d outside 1..4", s.s_q);
+    if (s.dtype != GQLA_BF16 && s.dtype != GQLA_F32) return fail(GQLA_ERR_INVALID_ARG, "unknown dtype %d", s.dtype);
+    if (batch < 1 || total_ctx < 1) return fail(GQLA_ERR_INVALID_ARG, "batch and total_ctx must be >= 1");
+    if (!(peak_flops > 0.0) || !std::isfinite(peak_flops) || !(peak_bytes_per_s > 0.0) || !std::isfinite(peak_bytes_per_s))
+        return fail(GQLA_ERR_INVALID_ARG, "peaks must be finite and > 0");
+    if (!choice) return fail(GQLA_ERR_INVALID_ARG, "choice is null");
+    const double e = s.dtype == GQLA_BF16 ? 2.0 : 4.0;
+    const double T = (double)total_ctx;
+    gqla_path_choice best{};
+    bool have = false;
+    for (int sq = 1; sq <= s.s_q; ++sq) {
+        for (int path = GQLA_PATH_ABSORB; path <= GQLA_PATH_GQA; ++path) {
+            const double bytes = path == GQLA_PATH_ABSORB ? e * (s.r_kv + s.d_r) : e * (2.0 * s.g * s.d_h + s.d_r);
+            const double flops = path == GQLA_PATH_ABSORB ? 2.0 * sq * s.h_q * (2.0 * s.r_kv + s.d_r)
+                                                          : 2.0 * sq * s.h_q * (2.0 * s.d_h + s.d_r);
+            const double t_mem = bytes * T / peak_bytes_per_s, t_cmp = flops * T / peak_flops;
+            const double tps = (double)batch * sq / std::max(t_mem, t_cmp);
+            if (!have || tps > best.tokens_per_s) {
+                best.path = path;
+                best.s_q = sq;
+                best.compute_bound = t_cmp > t_mem ? 1 : 0;
+                best.reserved = 0;
+                best.tokens_per_s = tps;
+                have = true;
+            }
+        }
+    }
+    *choice = best;
+    return ok();
+}
+
+gqla_status gqla_measure_peaks(void* scratch, size_t scratch_bytes, double* bytes_per_s, double* flops_per_s,
+                               void* stream) {
+    constexpr size_t kMin = size_t(64) << 20;
+    if (!bytes_per_s || !flops_per_s) return fail(GQLA_ERR_INVALID_ARG, "bytes_per_s or flops_per_s is null");
+    TRY(check_ptr(scratch, "scratch"));
+    if (scratch_bytes < kMin) return fail(GQLA_ERR_INVALID_ARG, "scratch of %zu bytes < 64 MiB", scratch_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int cus = device_cus();
+    TRY(hip_status(gqla::probe_read_bandwidth(scratch, scratch_bytes & ~size_t(15), cus, st, bytes_per_s),
+                   "read probe"));
+    return hip_status(gqla::probe_mfma_rate(scratch, cus, st, flops_per_s), "mfma probe");
 }
 
 gqla_status gqla_set_kernel_events(void* before, void* after) {

@@ -44,11 +44,22 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
     const int lane = tid & 63, wave = tid >> 6;
     const int q4 = lane >> 4, r16 = lane & 15;
 
+    // stage W_UK[j]: 8192 chunks of 16 bytes, 32 per thread, loaded 8 at a time so that
+    // eight loads are in flight per lane instead of one
     const u16* wj = w_uk + (size_t)j * DH * RK;
-    for (int c = tid; c < DH * (RK / 8); c += 256) {
-        const int d = c >> 6, r8 = c & 63;
-        *reinterpret_cast<u32x4*>(wt + d * PRO_STRIDE + r8 * 8) =
-            *reinterpret_cast<const u32x4*>(wj + (size_t)d * RK + r8 * 8);
+#pragma unroll
+    for (int c0 = 0; c0 < DH * (RK / 8); c0 += 8 * 256) {
+        u32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = c0 + k * 256 + tid;
+            v[k] = *reinterpret_cast<const u32x4*>(wj + (size_t)(c >> 6) * RK + (c & 63) * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = c0 + k * 256 + tid;
+            *reinterpret_cast<u32x4*>(wt + (c >> 6) * PRO_STRIDE + (c & 63) * 8) = v[k];
+        }
     }
     __syncthreads();
 

@@ -42,6 +42,27 @@ struct ExpandArgs {
     int64_t group_bstride;
 };
 
+// Decode-step append: new latent rows, rotated keys and queries, expanded new rows.
+struct AppendArgs {
+    int h_q, g, r_kv, d_r, d_h, s_q;
+    int batch, max_ctx;
+    float theta;
+    const void* c_new;                  // [batch][s_q][r_kv]
+    const void* kr_new;                 // [batch][s_q][d_r], before rotation
+    const void* q_rope_raw;             // [batch][s_q][h_q][d_r] or null
+    void* q_rope_out;                   // same shape, or null
+    const int32_t* ctx_lens;
+    void* latent;
+    int64_t latent_bstride;
+    const void* w_uk;                   // needed with group_cache
+    const void* w_uv;
+    void* group_cache;                  // or null
+    int64_t group_bstride;
+};
+
+hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_append_expand_bf16(const AppendArgs& a, hipStream_t st);
+
 // bf16 MFMA path (r_kv = 512, d_r = 64, d_h = 128)
 hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t st);
@@ -53,6 +74,10 @@ int absorb_block_rows(int query_rows);     // query rows per absorb workgroup (3
 hipError_t launch_absorb_f32(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_expand_f32(const ExpandArgs& a, hipStream_t st);
+
+// device peak probes (block the host until done)
+hipError_t probe_read_bandwidth(const void* buf, size_t bytes, int cus, hipStream_t st, double* bytes_per_s);
+hipError_t probe_mfma_rate(void* out, int cus, hipStream_t st, double* flops_per_s);
 
 // split-K log-sum-exp merge of the per-chunk partials into out / lse
 hipError_t launch_combine(const DecodeArgs& a, bool out_bf16, hipStream_t st);

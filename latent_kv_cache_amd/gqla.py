@@ -24,7 +24,8 @@ ABSORB, GQA = 0, 1
 STATUS = {0: "GQLA_OK", 1: "GQLA_ERR_INVALID_ARG", 2: "GQLA_ERR_UNSUPPORTED", 3: "GQLA_ERR_WORKSPACE", 4: "GQLA_ERR_HIP"}
 
 EXPORTS = ("gqla_workspace_size", "gqla_plan_splits", "gqla_expand_groups", "gqla_decode_absorb",
-           "gqla_decode_gqa", "gqla_set_kernel_events", "gqla_status_string", "gqla_last_error")
+           "gqla_decode_gqa", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
+           "gqla_set_kernel_events", "gqla_status_string", "gqla_last_error")
 
 
 class Shape(ctypes.Structure):
@@ -33,6 +34,13 @@ class Shape(ctypes.Structure):
     _fields_ = [("h_q", ctypes.c_int32), ("g", ctypes.c_int32), ("r_kv", ctypes.c_int32),
                 ("d_r", ctypes.c_int32), ("d_h", ctypes.c_int32), ("s_q", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class PathChoice(ctypes.Structure):
+    """Mirror of struct gqla_path_choice."""
+
+    _fields_ = [("path", ctypes.c_int32), ("s_q", ctypes.c_int32), ("compute_bound", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("tokens_per_s", ctypes.c_double)]
 
 
 class GQLAError(RuntimeError):
@@ -65,9 +73,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        c_vp, c_sz, c_i32, c_vp]
     lib.gqla_decode_gqa.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_sz,
                                     c_i32, c_vp]
+    lib.gqla_append_rows.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_i64,
+                                     c_vp, c_vp, c_vp, c_i64, c_vp]
+    lib.gqla_select_path.argtypes = [sp, c_i32, c_i64, ctypes.c_double, ctypes.c_double, ctypes.POINTER(PathChoice)]
+    lib.gqla_measure_peaks.argtypes = [c_vp, c_sz, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                       c_vp]
     lib.gqla_set_kernel_events.argtypes = [c_vp, c_vp]
     for name in ("gqla_workspace_size", "gqla_plan_splits", "gqla_expand_groups", "gqla_decode_absorb",
-                 "gqla_decode_gqa", "gqla_set_kernel_events"):
+                 "gqla_decode_gqa", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
+                 "gqla_set_kernel_events"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gqla_status_string.argtypes = [ctypes.c_int]
     lib.gqla_status_string.restype = ctypes.c_char_p
@@ -181,3 +195,37 @@ def decode_gqa(shape: Shape, q_nope, q_rope, group_cache, ctx_lens, out, lse=Non
                                   _ptr(group_cache), gbs, _ptr(ctx_lens), _ptr(out), _ptr(lse), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), num_splits, _stream(stream)))
     return out
+
+
+def append_rows(shape: Shape, c_new, kr_new, ctx_lens, latent, q_rope_raw=None, q_rope_out=None,
+                rope_theta: float = 10000.0, w_uk=None, w_uv=None, group_cache=None, stream=None):
+    """Decode-step append: write the s_q new rows of every sequence into latent [B][S][r_kv + d_r]
+    (c_new [B][s_q][r_kv], kr_new [B][s_q][d_r] rotated at t = L_b - s_q + s), rotate q_rope_raw
+    into q_rope_out, and expand the new rows into group_cache [B][S][2 g d_h + d_r] if given."""
+    lbs, max_ctx = _rows(latent, shape.r_kv + shape.d_r)
+    gbs = 0
+    if group_cache is not None:
+        gbs, gctx = _rows(group_cache, 2 * shape.g * shape.d_h + shape.d_r)
+        if gctx < max_ctx:
+            raise ValueError("group_cache holds fewer rows per sequence than latent")
+    _check(load().gqla_append_rows(ctypes.byref(shape), latent.shape[0], max_ctx, _ptr(c_new), _ptr(kr_new),
+                                   _ptr(q_rope_raw), _ptr(q_rope_out), float(rope_theta), _ptr(ctx_lens),
+                                   _ptr(latent), lbs, _ptr(w_uk), _ptr(w_uv), _ptr(group_cache), gbs,
+                                   _stream(stream)))
+
+
+def select_path(shape: Shape, batch: int, total_ctx: int, peak_flops: float, peak_bytes_per_s: float) -> PathChoice:
+    """Roofline choice of (path, s_q <= shape.s_q) for a step over contexts summing to total_ctx."""
+    ch = PathChoice()
+    _check(load().gqla_select_path(ctypes.byref(shape), batch, total_ctx, float(peak_flops), float(peak_bytes_per_s),
+                                   ctypes.byref(ch)))
+    return ch
+
+
+def measure_peaks(scratch, stream=None) -> Tuple[float, float]:
+    """(HBM read bytes/s, dense bf16 MFMA flop/s) of the current device; scratch is a device
+    tensor of at least 64 MiB whose contents are overwritten.  Waits for the measurement."""
+    bw, fl = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    _check(load().gqla_measure_peaks(_ptr(scratch), scratch.numel() * scratch.element_size(), ctypes.byref(bw),
+                                     ctypes.byref(fl), _stream(stream)))
+    return bw.value, fl.value

@@ -7,11 +7,13 @@ no code with the HIP library or its Python binding.
 """
 from .gqla import (  # noqa: F401
     absorb_decode,
+    append_rows,
     decode_batch,
     expand_groups,
     gqa_decode,
     group_of_head,
     lse_merge,
+    rope_rotate,
     split_partials,
     textbook_decode,
     visible_rows,

@@ -29,7 +29,12 @@ Readings where the page is silent (each is also listed in the design notes):
   selection), the s_q new tokens are the last s_q cached rows, and query s
   sees rows t <= L - s_q + s (causal among the new tokens);
 * a query that sees no row returns o = 0 and lse = -inf;
-* lse is the natural-log log-sum-exp of the scaled scores.
+* lse is the natural-log log-sum-exp of the scaled scores;
+* the decode-step append (``rope_rotate``, ``append_rows``), the step that
+  feeds the path, rotates with the half-split pairing (x_k, x_{k + d_R/2}) at
+  frequency theta^(-2k/d_R), theta = 10000 unless given; cache row t sits at
+  position t, so the s_q new tokens of a sequence of length L take positions
+  L - s_q .. L - 1, and their queries the same positions.
 
 Everything is computed in float64 from the stored (bf16- or fp32-rounded)
 inputs; nothing is blocked, fused or reordered beyond the definition.
@@ -254,3 +259,44 @@ def decode_batch(form: str, rows_of, q_nope, q_rope, w_uk, w_uv, lengths, scale:
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
+
+
+def rope_rotate(x, positions, theta: float = 10000.0) -> np.ndarray:
+    """Rotary embedding of vectors x [..., n][d_R] at integer positions [..., n] (float64).
+
+    Half-split pairing: component k < d_R/2 pairs with k + d_R/2 and the pair turns by
+    the angle position * theta^(-2k/d_R):
+        x'_k        = x_k cos a - x_{k+d/2} sin a
+        x'_{k+d/2}  = x_k sin a + x_{k+d/2} cos a
+    Section 2 (Architecture) keeps one shared rotary key per token and a rotary part
+    per query head; the rotation itself is the standard one, applied before attention.
+    """
+    x = np.asarray(x, F64)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("rotary width must be even")
+    half = d // 2
+    freq = theta ** (-2.0 * np.arange(half, dtype=F64) / d)                 # [half]
+    ang = np.asarray(positions, F64)[..., None] * freq                      # [..., half]
+    cos, sin = np.cos(ang), np.sin(ang)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * cos - b * sin, a * sin + b * cos], axis=-1)
+
+
+def append_rows(c_new, kr_raw, q_rope_raw, length: int, theta: float = 10000.0):
+    """The decode-step append of one sequence: its s_q new tokens enter the cache.
+
+    c_new       [s_q][r_kv]         new latent rows
+    kr_raw      [s_q][d_R]          new rotary keys before rotation
+    q_rope_raw  [s_q][h_q][d_R]     rotary query parts before rotation
+    length      L, the sequence length including the new tokens (L >= s_q)
+    returns (positions [s_q], cache rows [s_q][r_kv + d_R] = [c | rotated k_R],
+             rotated q_rope [s_q][h_q][d_R])
+    New token s sits at position L - s_q + s; its key and its queries are rotated there.
+    """
+    c_new = np.asarray(c_new, F64)
+    s_q = c_new.shape[0]
+    pos = np.arange(length - s_q, length, dtype=np.int64)
+    rows = np.concatenate([c_new, rope_rotate(kr_raw, pos, theta)], axis=1)
+    q_rot = rope_rotate(q_rope_raw, np.broadcast_to(pos[:, None], np.asarray(q_rope_raw).shape[:2]), theta)
+    return pos, rows, q_rot

@@ -251,4 +251,60 @@ def pin_expanded_row(orc):
         np.testing.assert_array_equal(gu[0, (g + j) * d_h:(g + j + 1) * d_h], p["w_uv"][j][:, 3])
 
 
+def pin_rope_closed_form(orc):
+    """Hand-computed rotations fix the pairing (k with k + d_R/2), the frequency
+    theta^(-2k/d_R) and the direction of the turn."""
+    # d_R = 2: the single pair turns by the position itself
+    np.testing.assert_allclose(orc.rope_rotate(np.array([1.0, 0.0]), 3), [math.cos(3), math.sin(3)], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(orc.rope_rotate(np.array([0.0, 1.0]), 3), [-math.sin(3), math.cos(3)], rtol=0, atol=1e-15)
+    # d_R = 4, theta = 10000: pair (x_1, x_3) turns at 10000^(-1/2) = 0.01 rad per position
+    x = np.array([0.0, 1.0, 0.0, 0.0])
+    np.testing.assert_allclose(orc.rope_rotate(x, 100), [0.0, math.cos(1.0), 0.0, math.sin(1.0)], rtol=0, atol=1e-14)
+    # pair (x_0, x_2) at frequency 1 and another base
+    x = np.array([2.0, 0.0, -1.0, 0.0])
+    a = 5.0
+    np.testing.assert_allclose(orc.rope_rotate(x, 5, theta=500.0),
+                               [2 * math.cos(a) + math.sin(a), 0.0, 2 * math.sin(a) - math.cos(a), 0.0], rtol=0, atol=1e-14)
+
+
+def pin_rope_rotation_properties(orc):
+    """Position 0 is the identity, every pair keeps its length, and scores depend only on
+    the distance between query and key positions (the defining property of rotary
+    embeddings): <R(p) q, R(t) k> = <R(p - t) q, k>."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((6, 16))
+    np.testing.assert_array_equal(orc.rope_rotate(x, np.zeros(6, dtype=np.int64)), x)
+    pos = rng.integers(0, 100000, 6)
+    y = orc.rope_rotate(x, pos)
+    np.testing.assert_allclose(x[:, :8] ** 2 + x[:, 8:] ** 2, y[:, :8] ** 2 + y[:, 8:] ** 2, rtol=1e-12)
+    q, k = rng.standard_normal(16), rng.standard_normal(16)
+    for p, t in ((7, 3), (1000, 999), (5, 40), (70000, 12)):
+        lhs = orc.rope_rotate(q, p) @ orc.rope_rotate(k, t)
+        rhs = orc.rope_rotate(q, p - t) @ k
+        assert abs(lhs - rhs) <= 1e-9 * (1 + abs(rhs)), (p, t, lhs, rhs)
+
+
+def pin_append_positions(orc):
+    """Appending s_q tokens at once equals appending them one at a time, and the cache
+    ends up holding every key rotated at its own row index; the new queries sit at the
+    positions of the new rows."""
+    rng = np.random.default_rng(22)
+    L, s_q, h_q, r_kv, d_r = 9, 3, 4, 6, 8
+    c = rng.standard_normal((L, r_kv))
+    kr = rng.standard_normal((L, d_r))
+    qr = rng.standard_normal((s_q, h_q, d_r))
+    pos, rows, q_rot = orc.append_rows(c[L - s_q:], kr[L - s_q:], qr, L)
+    assert list(pos) == [L - 3, L - 2, L - 1]
+    whole = np.concatenate([c, orc.rope_rotate(kr, np.arange(L))], axis=1)
+    np.testing.assert_array_equal(rows, whole[L - s_q:])
+    for s in range(s_q):
+        _, row1, q1 = orc.append_rows(c[L - s_q + s:L - s_q + s + 1], kr[L - s_q + s:L - s_q + s + 1],
+                                      qr[s:s + 1], L - s_q + s + 1)
+        np.testing.assert_array_equal(row1[0], rows[s])
+        np.testing.assert_array_equal(q1[0], q_rot[s])
+    # the newest query against the newest key: zero distance, so the rotary score is
+    # the unrotated dot product
+    np.testing.assert_allclose(q_rot[-1] @ rows[-1, r_kv:], qr[-1] @ kr[-1], rtol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

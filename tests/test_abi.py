@@ -156,6 +156,37 @@ def test_expand_argument_validation(lib):
                                 None) == 0
 
 
+def test_append_argument_validation(lib):
+    L = gqla.load()
+    sh = FLAG
+    S = 64
+    F = FAKE
+
+    def call(c=F, kr=F, qraw=F, qout=F + 4096, theta=10000.0, lens=F, lat=F, lbs=S * 576, wuk=F, wuv=F, gc=F,
+             gbs=S * 2112, batch=2, shape=sh):
+        return L.gqla_append_rows(ctypes.byref(shape), batch, S, c, kr, qraw, qout, theta, lens, lat, lbs, wuk, wuv,
+                                  gc, gbs, None)
+    assert call(theta=0.0) == 1
+    assert call(theta=float("inf")) == 1
+    assert call(qout=None) == 1                    # q_rope_raw without q_rope_out
+    assert call(qraw=None) == 1
+    assert call(qout=F) == 1                       # aliasing
+    assert call(c=None) == 1
+    assert call(kr=F + 8) == 1                     # misaligned
+    assert call(lens=None) == 1
+    assert call(lbs=S * 576 - 8) == 1
+    assert call(wuk=None) == 1                     # expansion needs the weights
+    assert call(gbs=S * 2112 - 8) == 1
+    assert call(shape=gqla.make_shape(128, 8, 512, 64, 128, 1, dtype=9)) == 1
+    odd = gqla.make_shape(16, 2, 64, 14, 32, 1, dtype=gqla.F32)
+    assert call(shape=odd, lbs=S * 78, gbs=S * 142) == 1     # odd rotary width
+    # the group layout is only checked when rows are expanded
+    g16 = gqla.make_shape(128, 16, 512, 64, 128, 1)
+    assert call(shape=g16, gbs=S * (2 * 16 * 128 + 64)) == 2
+    # nothing to append
+    assert call(batch=0) == 0
+
+
 def test_binding_raises_without_status_ok(lib):
     with pytest.raises(gqla.GQLAError):
         gqla.workspace_size(gqla.make_shape(128, 7, 512, 64, 128, 1), gqla.GQA, 1, 1)

@@ -27,6 +27,13 @@ MUTATIONS = [
     ("value block order swapped in expansion", "out[:, (g + j) * d_h:(g + j + 1) * d_h] = c @ w_uv[j].T",
      "out[:, (g + j) * d_h:(g + j + 1) * d_h] = c @ w_uk[j].T"),
     ("merge weights not renormalised", "/ np.where(finite, z, 1.0)[..., None]", ""),
+    ("RoPE pairs interleaved", "a, b = x[..., :half], x[..., half:]", "a, b = x[..., 0::2], x[..., 1::2]"),
+    ("RoPE frequency exponent halved", "freq = theta ** (-2.0 * np.arange(half, dtype=F64) / d)",
+     "freq = theta ** (-1.0 * np.arange(half, dtype=F64) / d)"),
+    ("RoPE turns the other way", "return np.concatenate([a * cos - b * sin, a * sin + b * cos], axis=-1)",
+     "return np.concatenate([a * cos + b * sin, -a * sin + b * cos], axis=-1)"),
+    ("appended rows one position late", "pos = np.arange(length - s_q, length, dtype=np.int64)",
+     "pos = np.arange(length - s_q + 1, length + 1, dtype=np.int64)"),
 ]
 
 
