@@ -57,7 +57,7 @@ typedef enum gqla_status {
 } gqla_status;
 
 typedef enum gqla_dtype { GQLA_BF16 = 0, GQLA_F32 = 1 } gqla_dtype;
-typedef enum gqla_path { GQLA_PATH_ABSORB = 0, GQLA_PATH_GQA = 1 } gqla_path;
+typedef enum gqla_path { GQLA_PATH_ABSORB = 0, GQLA_PATH_GQA = 1, GQLA_PATH_SPARSE = 2 } gqla_path;
 
 /* Model and step shape (section 2, Architecture): h_q query heads, g groups,
  * latent width r_kv, rotary key width d_r, per-group head width d_h, s_q query
@@ -72,7 +72,9 @@ typedef struct gqla_shape {
 
 /* Bytes of device workspace a decode call needs (split-K partials, and for the
  * absorb path the absorbed queries).  num_splits: 0 = automatic, else an upper
- * bound on context chunks per sequence.  Returns GQLA_OK and writes *bytes. */
+ * bound on context chunks per sequence.  For GQLA_PATH_SPARSE the max_ctx argument
+ * is the index-list length topk (the chunks split the list).  Returns GQLA_OK and
+ * writes *bytes. */
 gqla_status gqla_workspace_size(const gqla_shape* shape, int32_t path, int32_t batch,
                                 int32_t max_ctx, int32_t num_splits, size_t* bytes);
 
@@ -125,6 +127,22 @@ gqla_status gqla_decode_gqa(const gqla_shape* shape, int32_t batch, int32_t max_
                             const int32_t* ctx_lens, void* out, float* lse,
                             void* workspace, size_t workspace_bytes,
                             int32_t num_splits, void* stream);
+
+/* Sparse GQLA decode (section 2, Sparse GQLA: fine-grained sparse attention keeps the
+ * GQA path, since a group's h_q/g = 16 heads fill one 16-row matrix tile).  Query
+ * token s of every head of group j attends only to the rows listed in
+ * indices[b][s][j][0..topk) of the expanded cache; entries outside [0, L_b) or past
+ * the token's causal window t <= L_b - s_q + s are skipped (-1 pads a short list), and
+ * a row listed twice counts twice.  With no usable entry o = 0 and lse = -inf.
+ *   indices  device int32 [batch][s_q][g][topk]; topk >= 0
+ *   workspace: gqla_workspace_size(shape, GQLA_PATH_SPARSE, batch, topk, num_splits)
+ *   other arguments as in gqla_decode_gqa.  Any g dividing h_q is accepted. */
+gqla_status gqla_decode_gqa_sparse(const gqla_shape* shape, int32_t batch, int32_t max_ctx,
+                                   const void* q_nope, const void* q_rope,
+                                   const void* group_cache, int64_t group_bstride,
+                                   const int32_t* ctx_lens, const int32_t* indices, int32_t topk,
+                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   int32_t num_splits, void* stream);
 
 /* Decode-step append (the step that feeds both decode paths; section 2,
  * Architecture: one latent row and one shared rotary key per token, a rotary query

@@ -52,7 +52,8 @@ bool is_bf16_mfma_shape(const gqla_shape& s) { return s.r_kv == 512 && s.d_r == 
 gqla_status check_shape(const gqla_shape* sp, int path) {
     if (!sp) return fail(GQLA_ERR_INVALID_ARG, "shape is null");
     const gqla_shape& s = *sp;
-    if (path != GQLA_PATH_ABSORB && path != GQLA_PATH_GQA) return fail(GQLA_ERR_INVALID_ARG, "path %d is neither absorb (0) nor gqa (1)", path);
+    if (path != GQLA_PATH_ABSORB && path != GQLA_PATH_GQA && path != GQLA_PATH_SPARSE)
+        return fail(GQLA_ERR_INVALID_ARG, "path %d is none of absorb (0), gqa (1), sparse (2)", path);
     if (s.h_q <= 0 || s.g <= 0 || s.r_kv <= 0 || s.d_r <= 0 || s.d_h <= 0)
         return fail(GQLA_ERR_INVALID_ARG, "dims must be positive (h_q=%d g=%d r_kv=%d d_r=%d d_h=%d)", s.h_q, s.g, s.r_kv, s.d_r, s.d_h);
     if (s.h_q % s.g != 0) return fail(GQLA_ERR_INVALID_ARG, "h_q=%d is not a multiple of g=%d", s.h_q, s.g);
@@ -91,12 +92,17 @@ Plan plan(const gqla_shape& s, int path, int batch, int max_ctx, int num_splits)
         want = num_splits;
     } else {
         int units = batch > 0 ? batch : 1;
+        int per_cu = 1;                                 // work units wanted per compute unit
         if (s.dtype == GQLA_BF16 && path == GQLA_PATH_ABSORB) {
             const int rows = gqla::absorb_block_rows(s.s_q * s.h_q);
             units *= (s.s_q * s.h_q + rows - 1) / rows;
+        } else if (s.dtype == GQLA_BF16 && path == GQLA_PATH_SPARSE) {
+            // one wave per (sequence, query token, group, 16-head tile): aim at 8 waves per CU
+            units *= s.s_q * s.g * ((s.h_q / s.g + 15) / 16);
+            per_cu = 8;
         }
         const int cus = device_cus();
-        want = (cus + units - 1) / units;
+        want = (cus * per_cu + units - 1) / units;
         const int by_len = (ctx + 4095) / 4096;
         if (by_len > want) want = by_len;
     }
@@ -302,6 +308,66 @@ gqla_status gqla_decode_gqa(const gqla_shape* shape, int32_t batch, int32_t max_
                             int32_t num_splits, void* stream) {
     return decode_common(GQLA_PATH_GQA, shape, batch, max_ctx, q_nope, q_rope, nullptr, nullptr, group_cache,
                          group_bstride, ctx_lens, out, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+gqla_status gqla_decode_gqa_sparse(const gqla_shape* shape, int32_t batch, int32_t max_ctx, const void* q_nope,
+                                   const void* q_rope, const void* group_cache, int64_t group_bstride,
+                                   const int32_t* ctx_lens, const int32_t* indices, int32_t topk, void* out,
+                                   float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                   void* stream) {
+    TRY(check_shape(shape, GQLA_PATH_SPARSE));
+    TRY(check_sizes(batch, max_ctx));
+    if (topk < 0) return fail(GQLA_ERR_INVALID_ARG, "topk=%d < 0", topk);
+    if (num_splits < 0) return fail(GQLA_ERR_INVALID_ARG, "num_splits=%d < 0", num_splits);
+    const gqla_shape& s = *shape;
+    if (batch == 0) return ok();
+    TRY(check_ptr(q_nope, "q_nope"));
+    TRY(check_ptr(q_rope, "q_rope"));
+    TRY(check_ptr(group_cache, "group_cache"));
+    TRY(check_stride(group_bstride, 2LL * s.g * s.d_h + s.d_r, max_ctx, "group_bstride"));
+    if (!ctx_lens) return fail(GQLA_ERR_INVALID_ARG, "ctx_lens is null");
+    if (topk > 0 && !indices) return fail(GQLA_ERR_INVALID_ARG, "indices is null");
+    if (indices && (reinterpret_cast<uintptr_t>(indices) & 3u)) return fail(GQLA_ERR_INVALID_ARG, "indices is not 4-byte aligned");
+    TRY(check_ptr(out, "out"));
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(GQLA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+    const Plan p = plan(s, GQLA_PATH_SPARSE, batch, topk, num_splits);
+    const Layout lay = layout(s, GQLA_PATH_SPARSE, batch, p);
+    if (!workspace) return fail(GQLA_ERR_WORKSPACE, "workspace is null (%zu bytes needed)", lay.total);
+    if (!aligned16(workspace)) return fail(GQLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < lay.total)
+        return fail(GQLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, lay.total);
+    gqla::DecodeArgs a;
+    a.h_q = s.h_q;
+    a.g = s.g;
+    a.r_kv = s.r_kv;
+    a.d_r = s.d_r;
+    a.d_h = s.d_h;
+    a.s_q = s.s_q;
+    a.scale = s.scale;
+    a.batch = batch;
+    a.max_ctx = max_ctx;
+    a.n_split = p.n_split;
+    a.chunk = p.chunk;
+    a.q_nope = q_nope;
+    a.q_rope = q_rope;
+    a.w_uk = nullptr;
+    a.w_uv = nullptr;
+    a.cache = group_cache;
+    a.bstride = group_bstride;
+    a.ctx_lens = ctx_lens;
+    a.out = out;
+    a.lse = lse;
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+    a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
+    a.qhat = nullptr;
+    a.ev_before = g_ev_before;
+    a.ev_after = g_ev_after;
+    a.n_merge = p.n_split;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool bf16 = s.dtype == GQLA_BF16;
+    TRY(hip_status(gqla::launch_gqa_sparse(a, indices, topk, bf16, st), "sparse decode launch"));
+    return hip_status(gqla::launch_combine(a, bf16, st), "combine launch");
 }
 
 gqla_status gqla_append_rows(const gqla_shape* shape, int32_t batch, int32_t max_ctx, const void* c_new,

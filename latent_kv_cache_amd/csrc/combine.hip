@@ -9,7 +9,8 @@
 // applied per chunk, so the same merge serves both decode paths.
 //
 // One wave per query row (b, s, h); lanes stride the d_h outputs.  Chunks of
-// sequence b are those with p * chunk < L_b; the others were never written.
+// sequence b are those with p * chunk < L_b (the others were never written), or all
+// n_all chunks when n_all > 0 (the sparse path, whose chunks split an index list).
 #include "common.h"
 #include "launch.h"
 
@@ -20,15 +21,14 @@ namespace {
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, const int32_t* __restrict__ ctx_lens,
-    int max_ctx, int chunk, int batch, int s_q, int h_q, int d_h, void* __restrict__ out,
+    int max_ctx, int chunk, int n_all, int batch, int s_q, int h_q, int d_h, void* __restrict__ out,
     float* __restrict__ lse_out) {
     const int rows = batch * s_q * h_q;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const int b = row / (s_q * h_q);
-    const int L = clampi(ctx_lens[b], 0, max_ctx);
-    const int nvalid = (L + chunk - 1) / chunk;
+    const int nvalid = n_all > 0 ? n_all : (clampi(ctx_lens[b], 0, max_ctx) + chunk - 1) / chunk;
     const size_t plane = (size_t)rows;   // rows per chunk plane
 
     float m = kNegInf;
@@ -73,10 +73,10 @@ hipError_t launch_combine(const DecodeArgs& a, bool out_bf16, hipStream_t st) {
     dim3 grid((rows + 3) / 4);
     if (out_bf16) {
         hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, st, a.part_o, a.part_lse, a.ctx_lens, a.max_ctx,
-                           a.chunk, a.batch, a.s_q, a.h_q, a.d_h, a.out, a.lse);
+                           a.chunk, a.n_merge, a.batch, a.s_q, a.h_q, a.d_h, a.out, a.lse);
     } else {
         hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, st, a.part_o, a.part_lse, a.ctx_lens,
-                           a.max_ctx, a.chunk, a.batch, a.s_q, a.h_q, a.d_h, a.out, a.lse);
+                           a.max_ctx, a.chunk, a.n_merge, a.batch, a.s_q, a.h_q, a.d_h, a.out, a.lse);
     }
     return hipGetLastError();
 }

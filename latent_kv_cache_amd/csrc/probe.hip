@@ -16,22 +16,27 @@ namespace {
 constexpr int kReadThreads = 512;
 constexpr int kReadUnroll = 8;       // 16-byte loads in flight per lane
 
-// Streams [base, base + n16 * 16) once; lanes read 16 bytes each, kReadUnroll loads per
-// lane in flight.  The values only feed a comparison with a runtime value that never
-// holds (never_lane = -1), so nothing is stored but the loads cannot be dropped.
+// Streams [base, base + n16 * 16) once.  Block k reads its own contiguous span (the
+// access pattern of the decode kernels, one chunk of one sequence per workgroup);
+// lanes read 16 bytes each with kReadUnroll loads in flight.  The values only feed a
+// comparison with a runtime value that never holds (never_lane = -1), so nothing is
+// stored but the loads cannot be dropped.
 __global__ __launch_bounds__(kReadThreads) void read_probe_kernel(const u32x4* __restrict__ base, size_t n16,
                                                                   uint32_t* __restrict__ sink, int never_lane) {
     uint32_t acc = 0;
-    const size_t stride = (size_t)gridDim.x * kReadThreads;
-    size_t i = (size_t)blockIdx.x * kReadThreads + threadIdx.x;
-    for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+    const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const size_t lo = (size_t)blockIdx.x * per;
+    const size_t hi = lo + per < n16 ? lo + per : n16;
+    size_t i = lo + threadIdx.x;
+    constexpr size_t step = (size_t)kReadThreads;
+    for (; i + (kReadUnroll - 1) * step < hi; i += kReadUnroll * step) {
         u32x4 v[kReadUnroll];
 #pragma unroll
-        for (int k = 0; k < kReadUnroll; ++k) v[k] = base[i + k * stride];
+        for (int k = 0; k < kReadUnroll; ++k) v[k] = base[i + k * step];
 #pragma unroll
         for (int k = 0; k < kReadUnroll; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
     }
-    for (; i < n16; i += stride) {
+    for (; i < hi; i += step) {
         const u32x4 v = base[i];
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
@@ -67,7 +72,7 @@ hipError_t probe_read_bandwidth(const void* buf, size_t bytes, int cus, hipStrea
     for (int rep = 0; rep < 4 && e == hipSuccess; ++rep) {   // the first pass warms up
         e = hipEventRecord(e0, st);
         if (e != hipSuccess) break;
-        hipLaunchKernelGGL(read_probe_kernel, dim3(8 * cus), dim3(kReadThreads), 0, st, (const u32x4*)buf, n16,
+        hipLaunchKernelGGL(read_probe_kernel, dim3(2 * cus), dim3(kReadThreads), 0, st, (const u32x4*)buf, n16,
                            (uint32_t*)buf, -1);
         e = hipGetLastError();
         if (e == hipSuccess) e = hipEventRecord(e1, st);
@@ -87,7 +92,7 @@ hipError_t probe_mfma_rate(void* out, int cus, hipStream_t st, double* flops_per
     hipError_t e = hipEventCreate(&e0);
     if (e == hipSuccess) e = hipEventCreate(&e1);
     const int blocks = 8 * cus;            // 32 waves per CU
-    const int iters = 4096;
+    const int iters = 16384;             // about 4 ms: long enough for the clock to settle
     double best = 0.0;
     for (int rep = 0; rep < 4 && e == hipSuccess; ++rep) {
         e = hipEventRecord(e0, st);

@@ -20,11 +20,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgqla.so")
 
 BF16, F32 = 0, 1
-ABSORB, GQA = 0, 1
+ABSORB, GQA, SPARSE = 0, 1, 2
 STATUS = {0: "GQLA_OK", 1: "GQLA_ERR_INVALID_ARG", 2: "GQLA_ERR_UNSUPPORTED", 3: "GQLA_ERR_WORKSPACE", 4: "GQLA_ERR_HIP"}
 
 EXPORTS = ("gqla_workspace_size", "gqla_plan_splits", "gqla_expand_groups", "gqla_decode_absorb",
-           "gqla_decode_gqa", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
+           "gqla_decode_gqa", "gqla_decode_gqa_sparse", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
            "gqla_set_kernel_events", "gqla_status_string", "gqla_last_error")
 
 
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        c_vp, c_sz, c_i32, c_vp]
     lib.gqla_decode_gqa.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_sz,
                                     c_i32, c_vp]
+    lib.gqla_decode_gqa_sparse.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_vp,
+                                           c_vp, c_sz, c_i32, c_vp]
     lib.gqla_append_rows.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_i64,
                                      c_vp, c_vp, c_vp, c_i64, c_vp]
     lib.gqla_select_path.argtypes = [sp, c_i32, c_i64, ctypes.c_double, ctypes.c_double, ctypes.POINTER(PathChoice)]
@@ -80,7 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        c_vp]
     lib.gqla_set_kernel_events.argtypes = [c_vp, c_vp]
     for name in ("gqla_workspace_size", "gqla_plan_splits", "gqla_expand_groups", "gqla_decode_absorb",
-                 "gqla_decode_gqa", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
+                 "gqla_decode_gqa", "gqla_decode_gqa_sparse", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
                  "gqla_set_kernel_events"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gqla_status_string.argtypes = [ctypes.c_int]
@@ -194,6 +196,24 @@ def decode_gqa(shape: Shape, q_nope, q_rope, group_cache, ctx_lens, out, lse=Non
     _check(load().gqla_decode_gqa(ctypes.byref(shape), batch, max_ctx, _ptr(q_nope), _ptr(q_rope),
                                   _ptr(group_cache), gbs, _ptr(ctx_lens), _ptr(out), _ptr(lse), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), num_splits, _stream(stream)))
+    return out
+
+
+def decode_gqa_sparse(shape: Shape, q_nope, q_rope, group_cache, ctx_lens, indices, out, lse=None, workspace=None,
+                      num_splits: int = 0, stream=None):
+    """Sparse GQLA decode: query token s of group j attends to the rows listed in
+    indices [B][s_q][g][topk] (int32; -1 pads) of group_cache [B][S][2 g d_h + d_r]."""
+    gbs, max_ctx = _rows(group_cache, 2 * shape.g * shape.d_h + shape.d_r)
+    batch = group_cache.shape[0]
+    if indices.dim() != 4 or tuple(indices.shape[:3]) != (batch, shape.s_q, shape.g) or not indices.is_contiguous():
+        raise ValueError(f"indices must be a contiguous [B][s_q][g][topk] tensor, got {tuple(indices.shape)}")
+    topk = int(indices.shape[3])
+    if workspace is None:
+        workspace = alloc_workspace(shape, SPARSE, batch, topk, num_splits, group_cache.device)
+    _check(load().gqla_decode_gqa_sparse(ctypes.byref(shape), batch, max_ctx, _ptr(q_nope), _ptr(q_rope),
+                                         _ptr(group_cache), gbs, _ptr(ctx_lens), _ptr(indices), topk, _ptr(out),
+                                         _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         num_splits, _stream(stream)))
     return out
 
 

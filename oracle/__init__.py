@@ -14,6 +14,7 @@ from .gqla import (  # noqa: F401
     group_of_head,
     lse_merge,
     rope_rotate,
+    sparse_gqa_decode,
     split_partials,
     textbook_decode,
     visible_rows,

@@ -30,6 +30,12 @@ Readings where the page is silent (each is also listed in the design notes):
   sees rows t <= L - s_q + s (causal among the new tokens);
 * a query that sees no row returns o = 0 and lse = -inf;
 * lse is the natural-log log-sum-exp of the scaled scores;
+* sparse GQLA (section 2, Sparse GQLA: fine-grained sparse attention keeps the
+  GQA path because a group's h_q/g = 16 heads fill one 16-row matrix tile):
+  every query token s and group j has its own list of selected cached rows,
+  shared by the group's heads; a head attends to the listed rows only, each
+  listing counting once (a row listed twice weighs twice); entries outside
+  [0, L) or past the query's causal window are skipped;
 * the decode-step append (``rope_rotate``, ``append_rows``), the step that
   feeds the path, rotates with the half-split pairing (x_k, x_{k + d_R/2}) at
   frequency theta^(-2k/d_R), theta = 10000 unless given; cache row t sits at
@@ -300,3 +306,32 @@ def append_rows(c_new, kr_raw, q_rope_raw, length: int, theta: float = 10000.0):
     rows = np.concatenate([c_new, rope_rotate(kr_raw, pos, theta)], axis=1)
     q_rot = rope_rotate(q_rope_raw, np.broadcast_to(pos[:, None], np.asarray(q_rope_raw).shape[:2]), theta)
     return pos, rows, q_rot
+
+
+def sparse_gqa_decode(group_rows, q_nope, q_rope, g: int, indices, length: int, scale: float):
+    """Sparse GQLA over expanded rows (section 2, Sparse GQLA).
+
+    group_rows [>= L][2 g d_h + d_R] as produced by ``expand_groups``
+    indices    [s_q][g][topk] integer row indices; query token s of a head of group j
+               attends to the rows listed in indices[s][j] that lie in [0, L) and in its
+               causal window t <= L - s_q + s, each listing counting once
+    returns o [s_q][h_q][d_h], lse [s_q][h_q]  (float64; o = 0, lse = -inf with no row)
+    """
+    q_nope = np.asarray(q_nope, F64)
+    q_rope = np.asarray(q_rope, F64)
+    s_q, h_q, d_h = q_nope.shape
+    gr = np.asarray(group_rows[:length], F64)
+    k_r = gr[:, 2 * g * d_h:]
+    idx = np.asarray(indices)
+    o = np.zeros((s_q, h_q, d_h), F64)
+    lse = np.full((s_q, h_q), -np.inf, F64)
+    for j in range(g):
+        heads = _heads_of_group(j, h_q, g)
+        k_j = np.concatenate([gr[:, j * d_h:(j + 1) * d_h], k_r], axis=1)
+        v_j = gr[:, (g + j) * d_h:(g + j + 1) * d_h]
+        for s in range(s_q):
+            n = visible_rows(length, s_q, s)
+            sel = np.array([int(t) for t in idx[s, j] if 0 <= t < n], dtype=np.int64)
+            q = np.concatenate([q_nope[s, heads], q_rope[s, heads]], axis=1)
+            o[s, heads], lse[s, heads] = _softmax_attend(scale * (q @ k_j[sel].T), v_j[sel])
+    return o, lse

@@ -307,4 +307,98 @@ def pin_append_positions(orc):
     np.testing.assert_allclose(q_rot[-1] @ rows[-1, r_kv:], qr[-1] @ kr[-1], rtol=1e-12)
 
 
+def _sparse_problem(seed, h_q=8, g=2, length=11, s_q=1, topk=6):
+    p = small_problem(seed=seed, h_q=h_q, g=g, length=length, s_q=s_q)
+    rng = np.random.default_rng(seed + 100)
+    p["gr"] = rng.standard_normal((length + 3, 2 * g * p["w_uk"].shape[1] + p["q_rope"].shape[2]))
+    p["idx"] = rng.integers(0, length, size=(s_q, g, topk))
+    return p
+
+
+def _sp(orc, p, idx=None):
+    g = p["w_uk"].shape[0]
+    return orc.sparse_gqa_decode(p["gr"], p["q_nope"], p["q_rope"], g, p["idx"] if idx is None else idx,
+                                 p["length"], p["scale"])
+
+
+def pin_sparse_all_rows_is_dense(orc):
+    """Listing every visible row once gives the dense GQA form (and, over expanded rows,
+    the textbook form), for s_q = 1 and 2 and in any order."""
+    for s_q in (1, 2):
+        p = _sparse_problem(30 + s_q, s_q=s_q)
+        g = p["w_uk"].shape[0]
+        L = p["length"]
+        idx = np.stack([np.stack([np.random.default_rng(s * 7 + j).permutation(L) for j in range(g)])
+                        for s in range(s_q)])
+        o, lse = _sp(orc, p, idx)
+        od, ld = orc.gqa_decode(p["gr"], p["q_nope"], p["q_rope"], g, L, p["scale"])
+        np.testing.assert_allclose(o, od, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse, ld, rtol=1e-12)
+
+
+def pin_sparse_bruteforce(orc):
+    """Scalar loops over the listed rows (math.fsum) with repeated, out-of-range and
+    future indices in the lists."""
+    p = _sparse_problem(41, h_q=4, g=2, length=7, s_q=2, topk=9)
+    p["idx"][0, 0, :4] = [3, 3, -1, 6]          # a duplicate, an empty slot, a row past query 0's window
+    p["idx"][1, 1, :3] = [8, 0, 0]              # a row past L, a duplicate
+    o, lse = _sp(orc, p)
+    g, d_h = p["w_uk"].shape[0], p["w_uk"].shape[1]
+    L, s_q, h_q = p["length"], 2, 4
+    gr = p["gr"]
+    for s in range(s_q):
+        n = L - s_q + s + 1
+        for i in range(h_q):
+            j = i // (h_q // g)
+            q = list(p["q_nope"][s, i]) + list(p["q_rope"][s, i])
+            rows = [int(t) for t in p["idx"][s, j] if 0 <= t < n]
+            sc = []
+            for t in rows:
+                k = list(gr[t, j * d_h:(j + 1) * d_h]) + list(gr[t, 2 * g * d_h:])
+                sc.append(p["scale"] * math.fsum(a * b for a, b in zip(q, k)))
+            m = max(sc)
+            w = [math.exp(x - m) for x in sc]
+            z = math.fsum(w)
+            for d in range(d_h):
+                ref = math.fsum(wt * gr[t, (g + j) * d_h + d] for wt, t in zip(w, rows)) / z
+                assert abs(o[s, i, d] - ref) <= 1e-12 * (1 + abs(ref))
+            assert abs(lse[s, i] - (m + math.log(z))) <= 1e-12 * (1 + abs(m))
+
+
+def pin_sparse_single_and_empty(orc):
+    """One listed row: o is that row's value block and lse its score; no usable row:
+    o = 0, lse = -inf."""
+    p = _sparse_problem(42, topk=1)
+    g, d_h = p["w_uk"].shape[0], p["w_uk"].shape[1]
+    p["idx"][0, :, 0] = [5, 2]
+    o, lse = _sp(orc, p)
+    for i in range(8):
+        j = i // 4
+        t = p["idx"][0, j, 0]
+        np.testing.assert_array_equal(o[0, i], p["gr"][t, (g + j) * d_h:(g + j + 1) * d_h])
+        k = np.concatenate([p["gr"][t, j * d_h:(j + 1) * d_h], p["gr"][t, 2 * g * d_h:]])
+        q = np.concatenate([p["q_nope"][0, i], p["q_rope"][0, i]])
+        assert abs(lse[0, i] - p["scale"] * (q @ k)) <= 1e-12
+    o, lse = _sp(orc, p, np.full((1, g, 3), -1))
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def pin_sparse_duplicate_weight(orc):
+    """A row listed twice weighs as if its score were raised by ln 2."""
+    p = _sparse_problem(43, topk=3)
+    g, d_h = p["w_uk"].shape[0], p["w_uk"].shape[1]
+    idx = np.array([[[1, 4, 4], [2, 7, 7]]])
+    o, lse = _sp(orc, p, idx)
+    for i in range(8):
+        j = i // 4
+        q = np.concatenate([p["q_nope"][0, i], p["q_rope"][0, i]])
+        rows = idx[0, j, :2]
+        sc = np.array([p["scale"] * (q @ np.concatenate([p["gr"][t, j * d_h:(j + 1) * d_h], p["gr"][t, 2 * g * d_h:]]))
+                       for t in rows])
+        sc[1] += math.log(2.0)
+        w = np.exp(sc - sc.max())
+        ref = (w @ p["gr"][rows, (g + j) * d_h:(g + j + 1) * d_h]) / w.sum()
+        np.testing.assert_allclose(o[0, i], ref, rtol=1e-12, atol=1e-13)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -187,6 +187,35 @@ def test_append_argument_validation(lib):
     assert call(batch=0) == 0
 
 
+def test_sparse_argument_validation(lib):
+    L = gqla.load()
+    sh = FLAG
+    S, K = 64, 48
+    n = ctypes.c_size_t(0)
+    assert L.gqla_workspace_size(ctypes.byref(sh), gqla.SPARSE, 2, K, 0, ctypes.byref(n)) == 0
+    need = n.value
+    assert need >= 2 * 128 * 128 * 4
+
+    def call(qn=FAKE, gc=FAKE, gbs=S * 2112, lens=FAKE, idx=FAKE, topk=K, out=FAKE, lse=None, ws=FAKE, wsb=need,
+             splits=0, shape=sh, batch=2):
+        return L.gqla_decode_gqa_sparse(ctypes.byref(shape), batch, S, qn, FAKE, gc, gbs, lens, idx, topk, out, lse, ws,
+                                        wsb, splits, None)
+    assert call(topk=-1) == 1
+    assert call(idx=None) == 1
+    assert call(idx=FAKE + 2) == 1                 # misaligned int32 list
+    assert call(gbs=S * 2112 - 8) == 1
+    assert call(lens=None) == 1
+    assert call(qn=None) == 1
+    assert call(wsb=need - 1) == 3
+    assert call(ws=None) == 3
+    assert call(splits=-2) == 1
+    assert call(batch=0) == 0                      # nothing to do
+    # any g dividing h_q is accepted on this path (g = 16 has no dense GQA kernel)
+    g16 = gqla.make_shape(128, 16, 512, 64, 128, 1)
+    assert L.gqla_workspace_size(ctypes.byref(g16), gqla.SPARSE, 2, K, 0, ctypes.byref(n)) == 0
+    assert L.gqla_workspace_size(ctypes.byref(g16), gqla.GQA, 2, K, 0, ctypes.byref(n)) == 2
+
+
 def test_binding_raises_without_status_ok(lib):
     with pytest.raises(gqla.GQLAError):
         gqla.workspace_size(gqla.make_shape(128, 7, 512, 64, 128, 1), gqla.GQA, 1, 1)

@@ -32,6 +32,12 @@ MUTATIONS = [
      "freq = theta ** (-1.0 * np.arange(half, dtype=F64) / d)"),
     ("RoPE turns the other way", "return np.concatenate([a * cos - b * sin, a * sin + b * cos], axis=-1)",
      "return np.concatenate([a * cos + b * sin, -a * sin + b * cos], axis=-1)"),
+    ("sparse rows past L kept", "sel = np.array([int(t) for t in idx[s, j] if 0 <= t < n], dtype=np.int64)",
+     "sel = np.array([int(t) for t in idx[s, j] if 0 <= t < length + 1], dtype=np.int64)"),
+    ("sparse duplicates collapsed", "sel = np.array([int(t) for t in idx[s, j] if 0 <= t < n], dtype=np.int64)",
+     "sel = np.unique(np.array([int(t) for t in idx[s, j] if 0 <= t < n], dtype=np.int64))"),
+    ("sparse lists of the wrong group", "sel = np.array([int(t) for t in idx[s, j] if 0 <= t < n], dtype=np.int64)",
+     "sel = np.array([int(t) for t in idx[s, (j + 1) % g] if 0 <= t < n], dtype=np.int64)"),
     ("appended rows one position late", "pos = np.arange(length - s_q, length, dtype=np.int64)",
      "pos = np.arange(length - s_q + 1, length + 1, dtype=np.int64)"),
 ]
