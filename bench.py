@@ -111,6 +111,86 @@ def cpu_baseline(cfg, budget_s, gpu_out):
     return rec, parity
 
 
+def next_rows(gqla, rf, cfg, sh, w, gc, dev, warmup, steps):
+    """The steps around the decode path, on the flagship batch (not part of the metric):
+    sparse GQLA decode over 2048 listed rows per (sequence, group), the decode-step append
+    of one new token per sequence (rows, rotary keys and queries, expanded rows), and the
+    path the roofline selector picks from this device's measured peaks."""
+    import torch
+    B, S = cfg.batch, w.max_ctx
+    out = {}
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for e in (k0, k1):
+            e.record()
+        torch.cuda.synchronize()
+        kern, call = [], []
+        for _ in range(steps):
+            gqla.set_kernel_events(k0, k1)
+            c0.record()
+            fn()
+            c1.record()
+            gqla.set_kernel_events(None, None)
+            torch.cuda.synchronize()
+            kern.append(k0.elapsed_time(k1))
+            call.append(c0.elapsed_time(c1))
+        return sum(kern) / len(kern), sum(call) / len(call)
+
+    topk = 2048
+    gen = torch.Generator(device=dev).manual_seed(7)
+    idx = torch.rand((B, cfg.s_q, cfg.g, S), device=dev, generator=gen).argsort(dim=-1)[..., :topk].to(torch.int32)
+    idx = idx.contiguous()
+    o = torch.empty((B, cfg.s_q, cfg.h_q, cfg.d_h), dtype=torch.bfloat16, device=dev)
+    ws = gqla.alloc_workspace(sh, gqla.SPARSE, B, topk, 0, dev)
+    kern, call = timed(lambda: gqla.decode_gqa_sparse(sh, w.q_nope, w.q_rope, gc, w.ctx_lens, idx, o, None, ws))
+    # gathered K_j, V_j and k_R of every listed row, its index, queries in, outputs out
+    alg = (B * cfg.s_q * cfg.g * topk * ((2 * cfg.d_h + cfg.d_r) * 2 + 4)
+           + B * cfg.s_q * cfg.h_q * (cfg.d_h + cfg.d_r + cfg.d_h) * 2)
+    out["sparse_gqa"] = {"topk": topk, "kernel": "gqa_sparse_kernel", "kernel_ms": round(kern, 4),
+                         "call_ms": round(call, 4), "alg_bytes_per_launch": alg,
+                         "hbm_frac": round(alg / (kern * 1e-3) / rf.MI355X.bw, 4),
+                         "n_split": gqla.plan_splits(sh, gqla.SPARSE, B, topk, 0)[0]}
+    del idx, ws
+
+    g = torch.Generator(device=dev).manual_seed(8)
+    c_new = torch.randn((B, cfg.s_q, cfg.r_kv), device=dev, generator=g).to(torch.bfloat16)
+    kr = torch.randn((B, cfg.s_q, cfg.d_r), device=dev, generator=g).to(torch.bfloat16)
+    qraw = torch.randn((B, cfg.s_q, cfg.h_q, cfg.d_r), device=dev, generator=g).to(torch.bfloat16)
+    qrot = torch.empty_like(qraw)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+
+    def append():
+        gqla.append_rows(sh, c_new, kr, w.ctx_lens, w.latent, qraw, qrot, 10000.0, w.w_uk, w.w_uv, gc)
+    for _ in range(warmup):
+        append()
+    t0.record()
+    for _ in range(steps):
+        append()
+    t1.record()
+    torch.cuda.synchronize()
+    out["append"] = {"tokens": B * cfg.s_q, "ms": round(t0.elapsed_time(t1) / steps, 4), "with_group_rows": True}
+
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    bw, fl = gqla.measure_peaks(scratch)
+    del scratch
+    sel = {}
+    for max_sq in (1, 2):
+        shp = gqla.make_shape(cfg.h_q, cfg.g, cfg.r_kv, cfg.d_r, cfg.d_h, max_sq, cfg.scale, gqla.BF16)
+        ch = gqla.select_path(shp, B, int(w.lens.sum()), fl, bw)
+        sel[f"max_s_q={max_sq}"] = {"path": "absorb" if ch.path == gqla.ABSORB else "gqa", "s_q": ch.s_q,
+                                     "roofline_tokens_per_s": round(ch.tokens_per_s, 1),
+                                     "compute_bound": bool(ch.compute_bound)}
+    out["path_selector"] = {"measured_hbm_bytes_per_s": round(bw, 1), "measured_mfma_flops": round(fl, 1),
+                            "measured_ridge": round(fl / bw, 1), "choice": sel}
+    return out
+
+
 def main(argv=None):
     args = parse(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -245,6 +325,7 @@ def main(argv=None):
 
     cpu, parity = (None, None) if args.no_cpu_baseline else cpu_baseline(
         cfg, args.cpu_seconds, {"absorb": out_a, "gqa": out_g})
+    nxt = next_rows(gqla, rf, cfg, sh, w, gc, dev, args.warmup, K)
 
     rec = {
         "metric": METRIC,
@@ -262,6 +343,7 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": cpu,
         "expand_ms": round(expand_ms, 3),
+        "next": nxt,
         "parity": parity,
         "input_gen_s": round(t_gen, 1),
         "device": torch.cuda.get_device_name(dev),
