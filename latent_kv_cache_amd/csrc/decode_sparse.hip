@@ -109,29 +109,47 @@ __global__ __launch_bounds__(NWS * 64) void gqa_sparse_kernel(
     u16* vl = vt[wave];
     int* il = idx_lds[wave];
 
+    // The tile's 32 indices go through the wave's LDS slice; the next tile's are loaded one
+    // tile ahead.  Every row load below is unconditional (rows outside the sequence read
+    // row 0 and are zeroed or masked afterwards), so the compiler issues all of a tile's
+    // loads before it waits for any.
+    int next_idx = (lane < TT && k0 + lane < k1) ? ilist[k0 + lane] : -1;
     for (int kb = k0; kb < k1; kb += TT) {
-        // the tile's row indices; -1 past the list's chunk
-        if (lane < TT) il[lane] = kb + lane < k1 ? ilist[kb + lane] : -1;
+        if (lane < TT) il[lane] = next_idx;
+        next_idx = (lane < TT && kb + TT + lane < k1) ? ilist[kb + TT + lane] : -1;
         // LDS operations of one wave complete in order: the reads below see these writes
         const int t0 = il[r16], t1 = il[16 + r16];
         const u16* row0 = seq + (size_t)((t0 >= 0 && t0 < L) ? t0 : 0) * W;
         const u16* row1 = seq + (size_t)((t1 >= 0 && t1 < L) ? t1 : 0) * W;
-        floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+        bf16x8 ka[6], kc[6];
 #pragma unroll
         for (int kk = 0; kk < 6; ++kk) {
             const int col = kk < 4 ? j * DH + kk * 32 + q4 * 8 : 2 * g * DH + (kk - 4) * 32 + q4 * 8;
-            acc0 = mfma16(ld_bf16x8(row0 + col), qv[kk], acc0);
-            acc1 = mfma16(ld_bf16x8(row1 + col), qv[kk], acc1);
+            ka[kk] = ld_bf16x8(row0 + col);
+            kc[kk] = ld_bf16x8(row1 + col);
         }
-        // V_j rows of the tile into this wave's LDS slice: chunk c = 16 per row
+        // V_j rows of the tile: chunk c = 16 per row
+        constexpr int NV = TT * (DH / 8) / 64;
+        u32x4 vv[NV];
+        bool vok[NV];
 #pragma unroll
-        for (int k = 0; k < TT * (DH / 8) / 64; ++k) {
+        for (int k = 0; k < NV; ++k) {
             const int c = k * 64 + lane;
-            const int tok = c >> 4, c16 = c & 15;
-            const int t = il[tok];
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (t >= 0 && t < L) v = *reinterpret_cast<const u32x4*>(seq + (size_t)t * W + (g + j) * DH + c16 * 8);
-            *reinterpret_cast<u32x4*>(vl + tok * VSTRIDE + c16 * 8) = v;
+            const int t = il[c >> 4];
+            vok[k] = t >= 0 && t < L;
+            vv[k] = *reinterpret_cast<const u32x4*>(seq + (size_t)(vok[k] ? t : 0) * W + (g + j) * DH + (c & 15) * 8);
+        }
+        floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+        for (int kk = 0; kk < 6; ++kk) {
+            acc0 = mfma16(ka[kk], qv[kk], acc0);
+            acc1 = mfma16(kc[kk], qv[kk], acc1);
+        }
+        // into the wave's LDS slice, rows outside the list or the sequence as zeros
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int c = k * 64 + lane;
+            *reinterpret_cast<u32x4*>(vl + (c >> 4) * VSTRIDE + (c & 15) * 8) = vok[k] ? vv[k] : u32x4{0u, 0u, 0u, 0u};
         }
         // scores of the lane's slot tokens 16(e/4) + 4q4 + e%4 (the D layout of S^T)
         float sc[8];
