@@ -18,11 +18,15 @@ namespace gqla {
 
 namespace {
 
+// Loads are issued NB partials at a time with clamped, unconditional addresses (entries
+// past the last partial get weight 0), so a row's loads overlap instead of waiting for
+// one another.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, const int32_t* __restrict__ ctx_lens,
     int max_ctx, int chunk, int n_all, int batch, int s_q, int h_q, int d_h, void* __restrict__ out,
     float* __restrict__ lse_out) {
+    constexpr int NB = 4;
     const int rows = batch * s_q * h_q;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -30,22 +34,34 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int b = row / (s_q * h_q);
     const int nvalid = n_all > 0 ? n_all : (clampi(ctx_lens[b], 0, max_ctx) + chunk - 1) / chunk;
     const size_t plane = (size_t)rows;   // rows per chunk plane
+    const int dl = d_h - 1;
 
     float m = kNegInf;
-    for (int p = 0; p < nvalid; ++p) m = fmaxf(m, part_lse[(size_t)p * plane + row]);
+    for (int p0 = 0; p0 < nvalid; p0 += NB) {
+        float lp[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) lp[k] = part_lse[(size_t)min(p0 + k, nvalid - 1) * plane + row];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) m = fmaxf(m, lp[k]);
+    }
     float z = 0.f;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};   // d_h <= 256: lane handles d = lane + 64k
     if (m != kNegInf) {
-        for (int p = 0; p < nvalid; ++p) {
-            const float lp = part_lse[(size_t)p * plane + row];
-            if (lp == kNegInf) continue;
-            const float w = __expf(lp - m);
-            z += w;
-            const float* po = part_o + ((size_t)p * plane + row) * d_h;
+        for (int p0 = 0; p0 < nvalid; p0 += NB) {
+            float lp[NB], po[NB][4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int d = lane + 64 * k;
-                if (d < d_h) acc[k] += w * po[d];
+            for (int k = 0; k < NB; ++k) {
+                const size_t pr = (size_t)min(p0 + k, nvalid - 1) * plane + row;
+                lp[k] = part_lse[pr];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) po[k][q] = part_o[pr * d_h + min(lane + 64 * q, dl)];
+            }
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const float w = (p0 + k < nvalid && lp[k] != kNegInf) ? __expf(lp[k] - m) : 0.f;
+                z += w;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] += w * po[k][q];
             }
         }
     }
