@@ -223,3 +223,36 @@ def test_decode_step_end_to_end(gqla):
         return oracle.gqa_decode(gc_dev[b, :L].astype(np.float64), qn[b], q_dev[b], cfg.g, L, cfg.scale)
     gu.compare(cfg, out_a, lse_a, [0, 1], w.lens, "step absorb", ref=ref_absorb)
     gu.compare(cfg, out_g, lse_g, [0, 1], w.lens, "step gqa", ref=ref_gqa)
+
+
+def test_append_full_size(gqla):
+    """The benchmark's batch: 128 sequences of 8192 rows, one new token each, with the
+    group cache; only the new rows are read back."""
+    import torch
+    cfg = synth.config(3)
+    B, S = cfg.batch, 8192
+    lens = np.full(B, S, dtype=np.int32)
+    note("append full size: 128 x 8192, group rows")
+    c, kr, qr = _inputs(cfg, lens, 91)
+    w_uk, w_uv = synth.up_weights(cfg)
+    dt = torch.bfloat16
+    latent = torch.zeros((B, S, cfg.r_kv + cfg.d_r), dtype=dt, device="cuda")
+    group = torch.zeros((B, S, 2 * cfg.g * cfg.d_h + cfg.d_r), dtype=dt, device="cuda")
+    q_out = torch.empty((B, 1, cfg.h_q, cfg.d_r), dtype=dt, device="cuda")
+    gqla.append_rows(gu.shape_of(cfg, gqla), _dev(torch, c, dt), _dev(torch, kr, dt),
+                     _dev(torch, lens, torch.int32), latent, q_rope_raw=_dev(torch, qr, dt), q_rope_out=q_out,
+                     w_uk=_dev(torch, w_uk, dt), w_uv=_dev(torch, w_uv, dt), group_cache=group)
+    torch.cuda.synchronize()
+    lat = gu.host(latent[:, S - 1])
+    grp = gu.host(group[:, S - 1])
+    qo = gu.host(q_out)
+    assert float(latent[:, S - 2].abs().max()) == 0.0 and float(group[:, S - 2].abs().max()) == 0.0
+    gw = 2 * cfg.g * cfg.d_h
+    for b in range(B):
+        _, rows, q_rot = oracle.append_rows(c[b], kr[b], qr[b], S)
+        np.testing.assert_array_equal(lat[b, :cfg.r_kv], c[b, 0])
+        _close_to_ulp("bf16", lat[b:b + 1, cfg.r_kv:], rows[:, cfg.r_kv:], f"b={b} k_R", exact_frac=0.99)
+        _close_to_ulp("bf16", qo[b], q_rot, f"b={b} q_R", exact_frac=0.99)
+        stored = synth.bf16_round(oracle.expand_groups(lat[b:b + 1].astype(np.float64), w_uk, w_uv)).astype(np.float64)
+        assert np.all(np.abs(grp[b:b + 1, :gw] - stored[:, :gw]) <= 2.0 ** -7 * np.abs(stored[:, :gw]) + 1e-4)
+        np.testing.assert_array_equal(grp[b, gw:], lat[b, cfg.r_kv:])
