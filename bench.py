@@ -47,6 +47,14 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
+# sources whose digest a counter record in profiles/traffic.json must match
+KERNEL_SOURCES = {
+    "gqa_decode": ["latent_kv_cache_amd/csrc/decode_gqa.hip", "latent_kv_cache_amd/csrc/common.h"],
+    "absorb_decode": ["latent_kv_cache_amd/csrc/decode_absorb.hip", "latent_kv_cache_amd/csrc/common.h"],
+    "gqa_sparse": ["latent_kv_cache_amd/csrc/decode_sparse.hip", "latent_kv_cache_amd/csrc/common.h"],
+}
+
+
 def sources_digest(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -305,23 +313,22 @@ def main(argv=None):
              "gqa": path_rec(work_g, call_g, kern_g, split_g, "gqa_decode_kernel<8, 8>")}
 
     # dominant kernel: the longer of the two main attention kernels
-    kernel_src = ["latent_kv_cache_amd/csrc/decode_gqa.hip", "latent_kv_cache_amd/csrc/decode_absorb.hip",
-                  "latent_kv_cache_amd/csrc/common.h"]
-    digest = sources_digest(kernel_src)
+    digest_g = sources_digest(KERNEL_SOURCES["gqa_decode"])
+    digest_a = sources_digest(KERNEL_SOURCES["absorb_decode"])
     if kern_g >= kern_a:
         # bytes per launch: expanded rows of every cached token, queries in, outputs out
         alg = (rf.gqa_bytes_per_token(cfg.g, cfg.d_h, cfg.d_r) * total_ctx
                + q_tokens * cfg.h_q * (cfg.d_h + cfg.d_r + cfg.d_h) * 2)
         achieved = alg / (kern_g * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("gqa_decode", digest),
+                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("gqa_decode", digest_g),
                 "kernel": "gqa_decode_kernel<8, 8>", "alg_bytes_per_launch": alg, "avg_ms": round(kern_g, 4)}
     else:
         alg = (rf.absorb_bytes_per_token(cfg.r_kv, cfg.d_r) * total_ctx
                + q_tokens * cfg.h_q * (cfg.r_kv + cfg.d_r + cfg.d_h) * 2 + cfg.g * cfg.d_h * cfg.r_kv * 2)
         achieved = alg / (kern_a * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("absorb_decode", digest),
+                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("absorb_decode", digest_a),
                 "kernel": absorb_name, "alg_bytes_per_launch": alg, "avg_ms": round(kern_a, 4)}
 
     cpu, parity = (None, None) if args.no_cpu_baseline else cpu_baseline(

@@ -16,7 +16,8 @@ namespace {
 constexpr int kReadThreads = 512;
 constexpr int kReadUnroll = 8;       // 16-byte loads in flight per lane
 
-// Streams [base, base + n16 * 16) once.  Block k reads its own contiguous span (the
+// Streams [base, base + n16 * 16) once, with nontemporal loads (the policy of the
+// streaming decode kernel).  Block k reads its own contiguous span (the
 // access pattern of the decode kernels, one chunk of one sequence per workgroup);
 // lanes read 16 bytes each with kReadUnroll loads in flight.  The values only feed a
 // comparison with a runtime value that never holds (never_lane = -1), so nothing is
@@ -32,12 +33,12 @@ __global__ __launch_bounds__(kReadThreads) void read_probe_kernel(const u32x4* _
     for (; i + (kReadUnroll - 1) * step < hi; i += kReadUnroll * step) {
         u32x4 v[kReadUnroll];
 #pragma unroll
-        for (int k = 0; k < kReadUnroll; ++k) v[k] = base[i + k * step];
+        for (int k = 0; k < kReadUnroll; ++k) v[k] = __builtin_nontemporal_load(base + i + k * step);
 #pragma unroll
         for (int k = 0; k < kReadUnroll; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
     }
     for (; i < hi; i += step) {
-        const u32x4 v = base[i];
+        const u32x4 v = __builtin_nontemporal_load(base + i);
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
     if ((int)threadIdx.x == never_lane && acc == 0x9e3779b9u) sink[0] = acc;
