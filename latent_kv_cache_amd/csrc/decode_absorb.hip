@@ -28,37 +28,41 @@ constexpr int TT = 32;    // tokens per tile
 // operand type of the attention kernel's MFMA).  With the softmax scale and the
 // change of base folded into the query, the attention kernel's scores come out as
 // log2-domain logits and need no multiply.
-// grid = (row blocks of 64, g); block = 4 waves.  Rows of group j are numbered
-// iota = (b*s_q + s)*hpg + hh.  W_UK[j] ([d][r], 128 KB) is staged row-major in LDS;
-// the contraction runs over d, so the A operand (W_UK^T) is formed with transposing
-// LDS reads: 4 rows d x 16 columns r per 16-lane group.
+// grid = (row blocks of 64, g, 4 quarters of the latent columns); block = 4 waves.
+// Rows of group j are numbered iota = (b*s_q + s)*hpg + hh.  The block's quarter of
+// W_UK[j] ([d][r], 128 x 128, 32 KB) is staged row-major in LDS, so four blocks fit on
+// a CU; the contraction runs over d, so the A operand (W_UK^T) is formed with
+// transposing LDS reads: 4 rows d x 16 columns r per 16-lane group.  The blocks of the
+// first quarter also write the scaled q^R.
 // ---------------------------------------------------------------------------
-constexpr int PRO_STRIDE = RK + 16;
+constexpr int PRO_COLS = RK / 4;
+constexpr int PRO_STRIDE = PRO_COLS + 16;
 
 __global__ __launch_bounds__(256) void absorb_prologue_kernel(
     const u16* __restrict__ q_nope, const u16* __restrict__ q_rope, const u16* __restrict__ w_uk,
     u16* __restrict__ qhat, int batch, int h_q, int g, int s_q, float scale_log2) {
     __shared__ __attribute__((aligned(16))) u16 wt[DH * PRO_STRIDE];
     const int j = blockIdx.y;
+    const int r0 = blockIdx.z * PRO_COLS;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int q4 = lane >> 4, r16 = lane & 15;
 
-    // stage W_UK[j]: 8192 chunks of 16 bytes, 32 per thread, loaded 8 at a time so that
-    // eight loads are in flight per lane instead of one
-    const u16* wj = w_uk + (size_t)j * DH * RK;
+    // stage columns r0 .. r0+127 of W_UK[j]: 2048 chunks of 16 bytes, 8 per thread, all
+    // eight loads in flight before the first store
+    const u16* wj = w_uk + (size_t)j * DH * RK + r0;
+    constexpr int CPRW = PRO_COLS / 8;   // 16-byte chunks per staged row
+    {
+        u32x4 v[DH * CPRW / 256];
 #pragma unroll
-    for (int c0 = 0; c0 < DH * (RK / 8); c0 += 8 * 256) {
-        u32x4 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int c = c0 + k * 256 + tid;
-            v[k] = *reinterpret_cast<const u32x4*>(wj + (size_t)(c >> 6) * RK + (c & 63) * 8);
+        for (int k = 0; k < DH * CPRW / 256; ++k) {
+            const int c = k * 256 + tid;
+            v[k] = *reinterpret_cast<const u32x4*>(wj + (size_t)(c / CPRW) * RK + (c % CPRW) * 8);
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int c = c0 + k * 256 + tid;
-            *reinterpret_cast<u32x4*>(wt + (c >> 6) * PRO_STRIDE + (c & 63) * 8) = v[k];
+        for (int k = 0; k < DH * CPRW / 256; ++k) {
+            const int c = k * 256 + tid;
+            *reinterpret_cast<u32x4*>(wt + (c / CPRW) * PRO_STRIDE + (c % CPRW) * 8) = v[k];
         }
     }
     __syncthreads();
@@ -79,10 +83,10 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
 #pragma unroll
     for (int kd = 0; kd < DH / 32; ++kd) qb[kd] = ok ? ld_bf16x8(q_nope + qrow * DH + kd * 32 + q4 * 8) : zero_bf16x8();
 
-    // A operand lane (q4, r16), k-step kd: W_UK[32kd + 8q4 + e][16mt + r16], e = 0..7
+    // A operand lane (q4, r16), k-step kd: W_UK[32kd + 8q4 + e][r0 + 16mt + r16], e = 0..7
     const u16* abase = wt + (8 * q4 + (r16 >> 2)) * PRO_STRIDE + 4 * (r16 & 3);
 #pragma unroll 4
-    for (int mt = 0; mt < RK / 16; ++mt) {
+    for (int mt = 0; mt < PRO_COLS / 16; ++mt) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kd = 0; kd < DH / 32; ++kd) {
@@ -95,10 +99,10 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
             u32x2 o;
             o[0] = pack2h(acc[0] * scale_log2, acc[1] * scale_log2);
             o[1] = pack2h(acc[2] * scale_log2, acc[3] * scale_log2);
-            *reinterpret_cast<u32x2*>(dst + mt * 16 + q4 * 4) = o;
+            *reinterpret_cast<u32x2*>(dst + r0 + mt * 16 + q4 * 4) = o;
         }
     }
-    if (ok) {
+    if (ok && blockIdx.z == 0) {
         // q^R: 64 elements = 8 chunks of 16 bytes; lane group q4 scales chunks q4 and q4 + 4
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -513,7 +517,7 @@ int absorb_block_rows(int query_rows) { return query_rows <= 32 ? 32 : (query_ro
 hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st) {
     const int hpg = a.h_q / a.g;
     const int rows_per_group = a.batch * a.s_q * hpg;
-    dim3 pgrid((rows_per_group + 63) / 64, a.g);
+    dim3 pgrid((rows_per_group + 63) / 64, a.g, RK / PRO_COLS);
     hipLaunchKernelGGL(absorb_prologue_kernel, pgrid, dim3(256), 0, st,
                        (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.w_uk, (u16*)a.qhat,
                        a.batch, a.h_q, a.g, a.s_q, a.scale * kLog2e);
