@@ -72,6 +72,14 @@ def test_tiny_fp32_ragged_multi(gqla):
     both_paths(cfg, [256, 1, 0, 97], gqla, 2, max_ctx=256, what="tiny-ragged")
 
 
+@pytest.mark.parametrize("d_h", [48, 256])
+def test_fp32_head_widths(gqla, d_h):
+    """d_h = 48 and 256: the combine's one- and four-outputs-per-lane layouts (upper lanes
+    idle at 48), with three chunks per sequence so every row is merged."""
+    cfg = synth.config(1).with_(batch=2, d_h=d_h)
+    both_paths(cfg, [256, 77], gqla, 3, max_ctx=256, what=f"tiny d_h={d_h}")
+
+
 # ---------------------------------------------------------------- bf16 shapes at reduced batch/context
 @pytest.mark.parametrize("num_splits", [0, 1, 3])
 def test_llama3_shape(gqla, num_splits):
@@ -83,6 +91,24 @@ def test_llama3_shape(gqla, num_splits):
 def test_flagship_shape_ragged(gqla, num_splits):
     cfg = synth.config(3).with_(batch=3)
     both_paths(cfg, [1000, 8192, 31], gqla, num_splits, max_ctx=8192, what="cfg3")
+
+
+@pytest.mark.parametrize("g", [1, 2])
+def test_flagship_heads_few_groups(gqla, g):
+    """h_q = 128 with g = 1 (every head shares one K/V: the MQA special case, 320-wide
+    expanded rows) and g = 2, through the device expansion and both decode paths."""
+    cfg = synth.config(3, g=g).with_(batch=2)
+    both_paths(cfg, [1500, 77], gqla, 0, max_ctx=1536, what=f"g={g}")
+    # the chain against the textbook at the long sequence, where the stored rows' rounding averages out
+    both_paths(cfg, [1500, 77], gqla, 0, seqs=[0], max_ctx=1536, what=f"g={g} e2e", end_to_end=True)
+
+
+@pytest.mark.parametrize("g", [1, 16])
+def test_tiny_fp32_group_extremes(gqla, g):
+    """fp32 at g = 1 (MQA) and g = h_q = 16 (one head per group: MLA's per-head
+    up-projections)."""
+    cfg = synth.config(1, g=g).with_(batch=2)
+    both_paths(cfg, [256, 40], gqla, 2, max_ctx=256, what=f"tiny g={g}")
 
 
 @pytest.mark.parametrize("g,s_q", [(8, 2), (4, 1), (8, 1)])
