@@ -39,8 +39,8 @@ COPY_BYTES = 1 << 30       # plain device copy run once per bench (counter calib
 def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (CPU baseline and its sampled agreement check)")

@@ -79,12 +79,23 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
     const int RQ = s_q * h_q;
     u16* dst = qhat + ((size_t)b * RQ + (size_t)s * h_q + h) * W;
 
+    // k-slot e of lane group q4 in k-step kd is d = 32kd + 4q4 + e (e < 4) or
+    // 32kd + 16 + 4q4 + (e - 4): the transposing reads of the four lane groups then lie
+    // 4 rows apart, 32 banks at this row stride, so they do not conflict
     bf16x8 qb[DH / 32];
 #pragma unroll
-    for (int kd = 0; kd < DH / 32; ++kd) qb[kd] = ok ? ld_bf16x8(q_nope + qrow * DH + kd * 32 + q4 * 8) : zero_bf16x8();
+    for (int kd = 0; kd < DH / 32; ++kd) {
+        if (ok) {
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(q_nope + qrow * DH + kd * 32 + q4 * 4);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(q_nope + qrow * DH + kd * 32 + 16 + q4 * 4);
+            qb[kd] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        } else {
+            qb[kd] = zero_bf16x8();
+        }
+    }
 
-    // A operand lane (q4, r16), k-step kd: W_UK[32kd + 8q4 + e][r0 + 16mt + r16], e = 0..7
-    const u16* abase = wt + (8 * q4 + (r16 >> 2)) * PRO_STRIDE + 4 * (r16 & 3);
+    // A operand lane (q4, r16), k-step kd: W_UK[d(kd, q4, e)][r0 + 16mt + r16], e = 0..7
+    const u16* abase = wt + (4 * q4 + (r16 >> 2)) * PRO_STRIDE + 4 * (r16 & 3);
 #pragma unroll 4
     for (int mt = 0; mt < PRO_COLS / 16; ++mt) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -92,7 +103,7 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
         for (int kd = 0; kd < DH / 32; ++kd) {
             const u16* pa = abase + kd * 32 * PRO_STRIDE + mt * 16;
             const u32x2 lo = lds_read_tr16(pa);
-            const u32x2 hi = lds_read_tr16(pa + 4 * PRO_STRIDE);
+            const u32x2 hi = lds_read_tr16(pa + 16 * PRO_STRIDE);
             acc = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), qb[kd], acc);
         }
         if (ok) {
