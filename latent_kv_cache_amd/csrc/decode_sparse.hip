@@ -128,7 +128,10 @@ __global__ __launch_bounds__(NWS * 64) void gqa_sparse_kernel(
             ka[kk] = ld_bf16x8(row0 + col);
             kc[kk] = ld_bf16x8(row1 + col);
         }
-        // V_j rows of the tile: chunk c = 16 per row
+        // V_j rows of the tile: chunk c = 16 per row.  Nontemporal: a V_j row belongs to one
+        // group and is not read again this step (on MI355X 234 -> 217 us at 2048 rows per
+        // (b, j)); K_j and k_R keep the default policy, k_R because the other groups' lists
+        // re-read it through L2.
         constexpr int NV = TT * (DH / 8) / 64;
         u32x4 vv[NV];
         bool vok[NV];
@@ -137,7 +140,8 @@ __global__ __launch_bounds__(NWS * 64) void gqa_sparse_kernel(
             const int c = k * 64 + lane;
             const int t = il[c >> 4];
             vok[k] = t >= 0 && t < L;
-            vv[k] = *reinterpret_cast<const u32x4*>(seq + (size_t)(vok[k] ? t : 0) * W + (g + j) * DH + (c & 15) * 8);
+            vv[k] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(seq + (size_t)(vok[k] ? t : 0) * W + (g + j) * DH + (c & 15) * 8));
         }
         floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
