@@ -36,6 +36,25 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 COPY_BYTES = 1 << 30       # plain device copy run once per bench (counter calibration)
 
 
+# name -> (config id, overrides, description).  The flagship is the metric's workload; the
+# others are the remaining bf16 decode shapes, measured with the same step (both paths).
+WORKLOADS = {
+    "flagship": (3, {}, "gqla-decode-flagship: both paths, bf16, batch 128, h_q 128, g 8, r_kv 512, "
+                        "d_R 64, d_h 128, ctx 8192 uniform, s_q 1"),
+    "llama3-8b": (2, {}, "LLaMA-3-8B-derived shape: both paths, bf16, batch 64, h_q 32, g 8, ctx 4096 uniform, s_q 1"),
+    "mtp-g8-sq2": (4, {"g": 8, "s_q": 2}, "multi-token step: both paths, bf16, batch 256, h_q 128, g 8, s_q 2, "
+                                          "ctx ragged in [1024, 32768]"),
+    "mtp-g4-sq1": (4, {"g": 4, "s_q": 1}, "multi-token shape at g 4: both paths, bf16, batch 256, h_q 128, g 4, "
+                                          "s_q 1, ctx ragged in [1024, 32768]"),
+    "long-context": (5, {}, "long context split-K: both paths, bf16, batch 16, h_q 128, g 8, s_q 1, "
+                            "ctx ragged in [65536, 131072]"),
+}
+
+
+def note(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -44,6 +63,8 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (CPU baseline and its sampled agreement check)")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="flagship",
+                    help="decode workload (default: the flagship step the metric is quoted on)")
     return ap.parse_args(argv)
 
 
@@ -218,10 +239,14 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     gqla.load()
-    cfg = synth.config(3)
+    cfg_id, overrides, workload_desc = WORKLOADS[args.workload]
+    cfg = synth.config(cfg_id, **overrides)
+    flagship = args.workload == "flagship"
+    note(f"workload {args.workload}: generating inputs")
     t_gen = time.perf_counter()
     w = make_workload(cfg, device=dev)
     t_gen = time.perf_counter() - t_gen
+    note(f"inputs ready in {t_gen:.1f} s; expanding group rows")
     B, S = cfg.batch, w.max_ctx
     total_ctx = int(w.lens.sum())
     sh = gqla.make_shape(cfg.h_q, cfg.g, cfg.r_kv, cfg.d_r, cfg.d_h, cfg.s_q, cfg.scale, gqla.BF16)
@@ -255,10 +280,12 @@ def main(argv=None):
     def gqa():
         gqla.decode_gqa(sh, w.q_nope, w.q_rope, gc, w.ctx_lens, out_g, None, ws_g)
 
+    note("warm-up")
     for _ in range(args.warmup):
         absorb()
         gqa()
     torch.cuda.synchronize()
+    note("timed steps")
 
     K = args.steps
     mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -309,8 +336,9 @@ def main(argv=None):
 
     rq = cfg.s_q * cfg.h_q
     absorb_name = "absorb_decode_kernel<%d, 1>" % (2 if rq <= 32 else (4 if rq <= 64 else 8))
+    gqa_name = "gqa_decode_kernel<%d, 8>" % cfg.g
     paths = {"absorb": path_rec(work_a, call_a, kern_a, split_a, absorb_name),
-             "gqa": path_rec(work_g, call_g, kern_g, split_g, "gqa_decode_kernel<8, 8>")}
+             "gqa": path_rec(work_g, call_g, kern_g, split_g, gqa_name)}
 
     # dominant kernel: the longer of the two main attention kernels
     digest_g = sources_digest(KERNEL_SOURCES["gqa_decode"])
@@ -322,7 +350,7 @@ def main(argv=None):
         achieved = alg / (kern_g * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                 "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("gqa_decode", digest_g),
-                "kernel": "gqa_decode_kernel<8, 8>", "alg_bytes_per_launch": alg, "avg_ms": round(kern_g, 4)}
+                "kernel": gqa_name, "alg_bytes_per_launch": alg, "avg_ms": round(kern_g, 4)}
     else:
         alg = (rf.absorb_bytes_per_token(cfg.r_kv, cfg.d_r) * total_ctx
                + q_tokens * cfg.h_q * (cfg.r_kv + cfg.d_r + cfg.d_h) * 2 + cfg.g * cfg.d_h * cfg.r_kv * 2)
@@ -331,9 +359,10 @@ def main(argv=None):
                 "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("absorb_decode", digest_a),
                 "kernel": absorb_name, "alg_bytes_per_launch": alg, "avg_ms": round(kern_a, 4)}
 
+    note("CPU oracle baseline" if not args.no_cpu_baseline else "done timing")
     cpu, parity = (None, None) if args.no_cpu_baseline else cpu_baseline(
         cfg, args.cpu_seconds, {"absorb": out_a, "gqa": out_g})
-    nxt = next_rows(gqla, rf, cfg, sh, w, gc, dev, args.warmup, K)
+    nxt = next_rows(gqla, rf, cfg, sh, w, gc, dev, args.warmup, K) if flagship else None
 
     rec = {
         "metric": METRIC,
@@ -343,10 +372,9 @@ def main(argv=None):
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "gqla-decode-flagship: both paths, bf16, batch 128, h_q 128, g 8, r_kv 512, "
-                               "d_R 64, d_h 128, ctx 8192 uniform, s_q 1",
-                   "batch": B, "ctx": int(cfg.ctx[0]), "h_q": cfg.h_q, "g": cfg.g, "s_q": cfg.s_q,
-                   "paths": ["absorb", "gqa"]},
+        "config": {"workload": workload_desc,
+                   "batch": B, "ctx": int(cfg.ctx[0]) if cfg.ctx[0] == cfg.ctx[1] else [int(c) for c in cfg.ctx],
+                   "h_q": cfg.h_q, "g": cfg.g, "s_q": cfg.s_q, "paths": ["absorb", "gqa"]},
         "paths": paths,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -96,6 +96,13 @@ Plan plan(const gqla_shape& s, int path, int batch, int max_ctx, int num_splits)
         if (s.dtype == GQLA_BF16 && path == GQLA_PATH_ABSORB) {
             const int rows = gqla::absorb_block_rows(s.s_q * s.h_q);
             units *= (s.s_q * s.h_q + rows - 1) / rows;
+        } else if (s.dtype == GQLA_BF16 && path == GQLA_PATH_GQA) {
+            // one 32-row tile in flight per workgroup: narrow rows (small g) need several
+            // workgroups per CU to keep enough bytes in flight (measured at 8192 tokens:
+            // g = 2 0.56 -> 0.67 and g = 1 0.40 -> 0.50 of peak with 4 per CU; 7 per CU
+            // was slower again at g = 1)
+            const size_t tile = (size_t)gqla::kBf16TokenTile * (2 * s.g * s.d_h + s.d_r) * 2;
+            if (tile < (64u << 10)) per_cu = std::min(4, (int)(((140u << 10) + tile - 1) / tile));
         } else if (s.dtype == GQLA_BF16 && path == GQLA_PATH_SPARSE) {
             // one wave per (sequence, query token, group, 16-head tile): aim at 8 waves per CU
             units *= s.s_q * s.g * ((s.h_q / s.g + 15) / 16);

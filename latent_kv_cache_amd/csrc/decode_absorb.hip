@@ -280,7 +280,10 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     const int z = slot % nz;
     const int pair = (slot / nz) * 8 + xcd;
     if (pair >= n_split * batch) return;           // padding of the last group of 8
-    const int b = pair / n_split, p = pair - b * n_split;
+    // pair = p * batch + b: the sequence index varies fastest across XCDs, so ragged
+    // batches spread evenly (chunk-major numbering would put every sequence's first,
+    // always full, chunk on the same XCD when n_split is a multiple of 8)
+    const int p = pair / batch, b = pair - p * batch;
     const int L = clampi(ctx_lens[b], 0, max_ctx);
     const int t0 = p * chunk;
     if (t0 >= L) return;

@@ -135,16 +135,26 @@ __device__ __forceinline__ void store_tile(u16* lds, const u32x4 (&reg)[NLOAD], 
 }
 
 // ---------------------------------------------------------------------------
-// GQA decode.  grid = (n_split, batch, pair blocks); block = NW waves.  The
-// (group, 16-row tile) pairs of a sequence are numbered pair = j*RT + rt with
-// RT = ceil(rows_per_group / 16); block z handles pairs [z*NW, z*NW + NW).
+// GQA decode.  One-dimensional XCD-aware grid; block = NW waves.  Block id i runs on
+// XCD i % 8; its slot i / 8 gives the pair block z = slot % nz and the (sequence,
+// chunk) unit u = (slot / nz) * 8 + i % 8 = p * batch + b.  So the nz blocks that read
+// the same tiles are 8 ids apart (one XCD, dispatched together: the second read is an
+// L2 hit), and the sequence index varies fastest across XCDs, which spreads ragged
+// batches evenly (chunk-major numbering would put every sequence's first, always
+// full, chunk on the same XCD).
+// The (group, 16-row tile) pairs of a sequence are numbered pair = j*RT + rt with
+// RT = ceil(rows_per_group / 16).  A wave owns RPW consecutive row tiles of one group
+// (RPW divides RT): its K_j and V_j operand reads from LDS then feed RPW MFMAs each,
+// and with RPW = 2 the 16 pairs of s_q = 2 at 16 heads per group (or of 32 heads per
+// group at s_q = 2, g = 4) fit one block, which reads every tile from HBM once.
+// Block z handles waves units [z*NW, z*NW + NW) of the G * RT / RPW.
 // Rows of group j are numbered rho = s*hpg + hh (query token s, head j*hpg + hh).
 // ---------------------------------------------------------------------------
-template <int G, int NW>
+template <int G, int NW, int RPW>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
     const u16* __restrict__ q_nope, const u16* __restrict__ q_rope,
     const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
-    int max_ctx, int h_q, int s_q, int chunk, int batch, float scale_log2,
+    int max_ctx, int h_q, int s_q, int chunk, int n_split, int nz, int batch, float scale_log2,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
     constexpr int W = 2 * G * DH + DR;
     constexpr int STRIDE = W + 16;   // row stride = 8 x odd dwords mod 64 banks
@@ -152,7 +162,11 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
     constexpr int NLOAD = (TT * (W / 8) + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) u16 lds[TT * STRIDE];
 
-    const int p = blockIdx.x, b = blockIdx.y;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int zb = slot % nz;
+    const int unit = (slot / nz) * 8 + xcd;
+    if (unit >= n_split * batch) return;      // padding of the last group of 8
+    const int p = unit / batch, b = unit - p * batch;
     const int L = clampi(ctx_lens[b], 0, max_ctx);
     const int t0 = p * chunk;
     if (t0 >= L) return;                      // uniform over the block
@@ -165,34 +179,45 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
     const int hpg = h_q / G;
     const int rows_g = s_q * hpg;
     const int RT = (rows_g + 15) >> 4;
-    const int pair = blockIdx.z * NW + wave;
-    const bool active = pair < G * RT;
-    const int j = active ? pair / RT : 0;
-    const int rt = active ? pair - j * RT : 0;
-    const int rho = rt * 16 + r16;
-    const bool row_ok = active && rho < rows_g;
-    const int s = row_ok ? rho / hpg : 0;
-    const int h = j * hpg + (row_ok ? rho - s * hpg : 0);
-    const int nvis = clampi(L - s_q + s + 1, 0, L);
-    const int qrow = (b * s_q + s) * h_q + h;
-
-    // queries as the B operand of S^T = K Q^T: k-steps 0..3 over q^N, 4..5 over q^R
-    f16x8 qv[6];
+    const int wu = zb * NW + wave;             // wave unit: RPW row tiles of one group
+    const bool active = wu * RPW < G * RT;
+    const int j = active ? (wu * RPW) / RT : 0;
+    const int rt0 = active ? wu * RPW - j * RT : 0;
+    bool row_ok[RPW];
+    int nvis[RPW], qrow[RPW];
 #pragma unroll
-    for (int kk = 0; kk < 6; ++kk) {
-        if (row_ok) {
-            const u16* src = kk < 4 ? q_nope + (size_t)qrow * DH + kk * 32 + q4 * 8
-                                    : q_rope + (size_t)qrow * DR + (kk - 4) * 32 + q4 * 8;
-            qv[kk] = as_f16x8(bf8_to_h8(*reinterpret_cast<const u32x4*>(src)));
-        } else {
-            qv[kk] = zero_f16x8();
-        }
+    for (int rg = 0; rg < RPW; ++rg) {
+        const int rho = (rt0 + rg) * 16 + r16;
+        row_ok[rg] = active && rho < rows_g;
+        const int s = row_ok[rg] ? rho / hpg : 0;
+        const int h = j * hpg + (row_ok[rg] ? rho - s * hpg : 0);
+        nvis[rg] = clampi(L - s_q + s + 1, 0, L);
+        qrow[rg] = (b * s_q + s) * h_q + h;
     }
 
-    floatx4 oacc[DH / 16];
+    // queries as the B operand of S^T = K Q^T: k-steps 0..3 over q^N, 4..5 over q^R
+    f16x8 qv[RPW][6];
 #pragma unroll
-    for (int n = 0; n < DH / 16; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
-    SoftmaxState st{kNegInf, 0.f};
+    for (int rg = 0; rg < RPW; ++rg)
+#pragma unroll
+        for (int kk = 0; kk < 6; ++kk) {
+            if (row_ok[rg]) {
+                const u16* src = kk < 4 ? q_nope + (size_t)qrow[rg] * DH + kk * 32 + q4 * 8
+                                        : q_rope + (size_t)qrow[rg] * DR + (kk - 4) * 32 + q4 * 8;
+                qv[rg][kk] = as_f16x8(bf8_to_h8(*reinterpret_cast<const u32x4*>(src)));
+            } else {
+                qv[rg][kk] = zero_f16x8();
+            }
+        }
+
+    floatx4 oacc[RPW][DH / 16];
+#pragma unroll
+    for (int rg = 0; rg < RPW; ++rg)
+#pragma unroll
+        for (int n = 0; n < DH / 16; ++n) oacc[rg][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    SoftmaxState st[RPW];
+#pragma unroll
+    for (int rg = 0; rg < RPW; ++rg) st[rg] = SoftmaxState{kNegInf, 0.f};
 
     const u16* seq = cache + (size_t)b * bstride;
     u32x4 reg[NLOAD];
@@ -209,74 +234,94 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
         }
         if (!active) continue;
 
-        float sc[8];
+        f16x8 pb[RPW];
         {
-            // two independent accumulator chains per 16-token half
-            floatx4 acc[2][2] = {};
+            // two independent accumulator chains per 16-token half and row tile
+            floatx4 acc[RPW][2][2] = {};
 #pragma unroll
             for (int kk = 0; kk < 6; ++kk) {
                 const int col = kk < 4 ? j * DH + kk * 32 + q4 * 8 : 2 * G * DH + (kk - 4) * 32 + q4 * 8;
 #pragma unroll
-                for (int th = 0; th < 2; ++th)
-                    acc[th][kk & 1] = mfma16h(ld_f16x8(lds + (th * 16 + r16) * STRIDE + col), qv[kk], acc[th][kk & 1]);
+                for (int th = 0; th < 2; ++th) {
+                    const f16x8 a = ld_f16x8(lds + (th * 16 + r16) * STRIDE + col);
+#pragma unroll
+                    for (int rg = 0; rg < RPW; ++rg)
+                        acc[rg][th][kk & 1] = mfma16h(a, qv[rg][kk], acc[rg][th][kk & 1]);
+                }
             }
 #pragma unroll
-            for (int th = 0; th < 2; ++th) {
+            for (int rg = 0; rg < RPW; ++rg) {
+                float sc[8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = tb + th * 16 + q4 * 4 + i;
-                    const float v = acc[th][0][i] + acc[th][1][i];
-                    sc[th * 4 + i] = (row_ok && t < t1 && t < nvis) ? v * scale_log2 : kNegInf;
+                for (int th = 0; th < 2; ++th) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = tb + th * 16 + q4 * 4 + i;
+                        const float v = acc[rg][th][0][i] + acc[rg][th][1][i];
+                        sc[th * 4 + i] = (row_ok[rg] && t < t1 && t < nvis[rg]) ? v * scale_log2 : kNegInf;
+                    }
+                }
+                bool rescale;
+                float alpha;
+                pb[rg] = softmax_tile(st[rg], sc, rescale, alpha);
+                if (__builtin_expect(rescale, 0)) {
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int n = 0; n < DH / 16; ++n) oacc[rg][n] *= alpha;
                 }
             }
         }
-        bool rescale;
-        float alpha;
-        const f16x8 pb = softmax_tile(st, sc, rescale, alpha);
-        if (__builtin_expect(rescale, 0)) {
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int n = 0; n < DH / 16; ++n) oacc[n] *= alpha;
-        }
         const int vcol = (G + j) * DH;
 #pragma unroll
-        for (int n = 0; n < DH / 16; ++n)
-            oacc[n] = mfma16h(gather_col(lds, STRIDE, q4, r16, vcol + 16 * n), pb, oacc[n]);
-    }
-    if (!row_ok) return;
-
-    const float l = wave_sum16x4(st.l);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
-    float* po = part_o + prow * DH;
+        for (int n = 0; n < DH / 16; ++n) {
+            const f16x8 a = gather_col(lds, STRIDE, q4, r16, vcol + 16 * n);
 #pragma unroll
-    for (int n = 0; n < DH / 16; ++n) {
-        *reinterpret_cast<floatx4*>(po + 16 * n + 4 * q4) = oacc[n] * inv;
+            for (int rg = 0; rg < RPW; ++rg) oacc[rg][n] = mfma16h(a, pb[rg], oacc[rg][n]);
+        }
     }
-    if (q4 == 0) part_lse[prow] = l > 0.f ? (st.m + __log2f(l)) * kLn2 : kNegInf;
+
+#pragma unroll
+    for (int rg = 0; rg < RPW; ++rg) {
+        // the four lanes of a row share row_ok, so the reduction runs over active lanes
+        if (!row_ok[rg]) continue;
+        const float l = wave_sum16x4(st[rg].l);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const size_t prow = (size_t)p * batch * s_q * h_q + qrow[rg];
+        float* po = part_o + prow * DH;
+#pragma unroll
+        for (int n = 0; n < DH / 16; ++n) *reinterpret_cast<floatx4*>(po + 16 * n + 4 * q4) = oacc[rg][n] * inv;
+        if (q4 == 0) part_lse[prow] = l > 0.f ? (st[rg].m + __log2f(l)) * kLn2 : kNegInf;
+    }
 }
 
-template <int G, int NW>
+template <int G, int NW, int RPW>
 hipError_t launch_gqa_t(const DecodeArgs& a, hipStream_t st) {
     const int rows_g = a.s_q * (a.h_q / a.g);
-    const int pairs = G * ((rows_g + 15) / 16);
-    dim3 grid(a.n_split, a.batch, (pairs + NW - 1) / NW);
+    const int waves = G * ((rows_g + 15) / 16) / RPW;
+    const int nz = (waves + NW - 1) / NW;
+    const int units = a.n_split * a.batch;
+    dim3 grid(((units + 7) / 8) * 8 * nz);
     hipError_t e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gqa_decode_kernel<G, NW>), grid, dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((gqa_decode_kernel<G, NW, RPW>), grid, dim3(NW * 64), 0, st,
                        (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.cache, a.bstride,
-                       a.ctx_lens, a.max_ctx, a.h_q, a.s_q, a.chunk, a.batch, a.scale * kLog2e,
+                       a.ctx_lens, a.max_ctx, a.h_q, a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e,
                        a.part_o, a.part_lse);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return record_if(a.ev_after, st);
 }
 
-// 8 waves per block: with 1024-thread blocks the 128-register cap spills the
-// staging registers; extra (group, row tile) pairs go to further blocks in z.
+// 8 waves per block (with 1024-thread blocks the 128-register cap spills the staging
+// registers).  Two row tiles per wave when a group has an even number of them and one
+// tile per wave would take more than one block, for g <= 4: at g = 8 the 2112-wide
+// tile's staging registers plus two tiles' state exceed 256 (47 spills), so there the
+// second block of pairs re-reads the tiles, through L2 when it keeps pace.
 template <int G>
 hipError_t launch_gqa_g(const DecodeArgs& a, hipStream_t st) {
-    return launch_gqa_t<G, 8>(a, st);
+    const int rt = (a.s_q * (a.h_q / a.g) + 15) / 16;
+    if (G <= 4 && rt % 2 == 0 && G * rt > 8) return launch_gqa_t<G, 8, 2>(a, st);
+    return launch_gqa_t<G, 8, 1>(a, st);
 }
 
 }  // namespace
