@@ -280,10 +280,12 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     const int z = slot % nz;
     const int pair = (slot / nz) * 8 + xcd;
     if (pair >= n_split * batch) return;           // padding of the last group of 8
-    // pair = p * batch + b: the sequence index varies fastest across XCDs, so ragged
-    // batches spread evenly (chunk-major numbering would put every sequence's first,
-    // always full, chunk on the same XCD when n_split is a multiple of 8)
-    const int p = pair / batch, b = pair - p * batch;
+    // pair = p * batch + bb with b = (bb + p) mod batch: the sequence index varies fastest
+    // across XCDs and chunk p of sequence b runs on XCD (b + p) % 8, so ragged batches
+    // spread evenly (chunk-major numbering would put every sequence's first, always full,
+    // chunk on the same XCD when n_split is a multiple of 8)
+    const int p = pair / batch, bb = pair - p * batch;
+    const int b = bb + p % batch < batch ? bb + p % batch : bb + p % batch - batch;
     const int L = clampi(ctx_lens[b], 0, max_ctx);
     const int t0 = p * chunk;
     if (t0 >= L) return;

@@ -137,11 +137,11 @@ __device__ __forceinline__ void store_tile(u16* lds, const u32x4 (&reg)[NLOAD], 
 // ---------------------------------------------------------------------------
 // GQA decode.  One-dimensional XCD-aware grid; block = NW waves.  Block id i runs on
 // XCD i % 8; its slot i / 8 gives the pair block z = slot % nz and the (sequence,
-// chunk) unit u = (slot / nz) * 8 + i % 8 = p * batch + b.  So the nz blocks that read
-// the same tiles are 8 ids apart (one XCD, dispatched together: the second read is an
-// L2 hit), and the sequence index varies fastest across XCDs, which spreads ragged
-// batches evenly (chunk-major numbering would put every sequence's first, always
-// full, chunk on the same XCD).
+// chunk) unit u = (slot / nz) * 8 + i % 8 = p * batch + bb, sequence b = (bb + p) mod
+// batch.  So the nz blocks that read the same tiles are 8 ids apart (one XCD,
+// dispatched together: the second read is an L2 hit), and chunk p of sequence b runs
+// on XCD (b + p) % 8, which spreads ragged batches evenly (chunk-major numbering would
+// put every sequence's first, always full, chunk on the same XCD).
 // The (group, 16-row tile) pairs of a sequence are numbered pair = j*RT + rt with
 // RT = ceil(rows_per_group / 16).  A wave owns RPW consecutive row tiles of one group
 // (RPW divides RT): its K_j and V_j operand reads from LDS then feed RPW MFMAs each,
@@ -166,7 +166,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
     const int zb = slot % nz;
     const int unit = (slot / nz) * 8 + xcd;
     if (unit >= n_split * batch) return;      // padding of the last group of 8
-    const int p = unit / batch, b = unit - p * batch;
+    // chunk p of sequence b runs on XCD (b + p) % 8 (batch a multiple of 8), so every XCD
+    // gets an even share of each chunk position
+    const int p = unit / batch, bb = unit - p * batch;
+    const int b = bb + p % batch < batch ? bb + p % batch : bb + p % batch - batch;
     const int L = clampi(ctx_lens[b], 0, max_ctx);
     const int t0 = p * chunk;
     if (t0 >= L) return;                      // uniform over the block
