@@ -104,14 +104,14 @@ __device__ __forceinline__ f16x8 gather_col(const u16* lds, int stride, int q4, 
 // The loads are nontemporal: every expanded row is read exactly once per decode step, and
 // on MI355X the streaming hint lifts this kernel from about 6.1 to 6.9 TB/s (same data,
 // same results).
-template <int W, int NT, int NLOAD>
+template <int W, int NT, int NLOAD, int ROWS = TT>
 __device__ __forceinline__ void load_tile(u32x4 (&reg)[NLOAD], const u16* __restrict__ base, int nrows, int tid) {
     constexpr int CPR = W / 8;   // 16-byte chunks per row
 #pragma unroll
     for (int k = 0; k < NLOAD; ++k) {
         const int c = tid + k * NT;
         const int r = c / CPR;
-        if (c < TT * CPR && r < nrows) {
+        if (c < ROWS * CPR && r < nrows) {
             reg[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)c * 8));
         } else {
             reg[k] = u32x4{0u, 0u, 0u, 0u};
@@ -120,13 +120,13 @@ __device__ __forceinline__ void load_tile(u32x4 (&reg)[NLOAD], const u16* __rest
 }
 
 // Store the staged tile into LDS as fp16 (bf16 -> fp16 conversion per element).
-template <int W, int STRIDE, int NT, int NLOAD>
+template <int W, int STRIDE, int NT, int NLOAD, int ROWS = TT>
 __device__ __forceinline__ void store_tile(u16* lds, const u32x4 (&reg)[NLOAD], int tid) {
     constexpr int CPR = W / 8;
 #pragma unroll
     for (int k = 0; k < NLOAD; ++k) {
         const int c = tid + k * NT;
-        if (c < TT * CPR) {
+        if (c < ROWS * CPR) {
             const int r = c / CPR;
             const int col = c - r * CPR;
             *reinterpret_cast<u32x4*>(lds + r * STRIDE + col * 8) = bf8_to_h8(reg[k]);
@@ -297,6 +297,195 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16-token tiles, for g = 8 with two row tiles per wave (s_q = 2 at 16 heads per
+// group).  Half-height tiles halve the staging registers and the score accumulators,
+// which is what lets one wave hold two row tiles' queries, accumulators and softmax
+// state at g = 8 within 256 registers; one block then covers all 16 (group, row tile)
+// pairs and reads every tile from HBM once.  The scores use the 16x16x32 MFMA over
+// K = d_h + d_R as above (one 16-token half); the value product uses the 16x16x16
+// fp16 MFMA, whose B operand (16 tokens x 16 rows) is the lane's own four softmax
+// weights in the D layout of the score tile, and whose A operand (16 features x 16
+// tokens) is one transposing LDS read.  The kernel stays HBM-bound: the half-rate
+// value MFMA has ample slack.  Grid, split-K and outputs as gqa_decode_kernel.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x4 softmax_tile4(SoftmaxState& st, float (&sc)[4], bool& rescale, float& alpha) {
+    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mt = wave_max16x4(mt);
+    const bool raise = mt > st.m + kLazy;
+    rescale = __any(raise);
+    alpha = 1.f;
+    if (raise) {
+        alpha = fast_exp2(st.m - mt);
+        st.l *= alpha;
+        st.m = mt;
+    }
+    const float muse = (st.m == kNegInf) ? 0.f : st.m;
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - muse);
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
+    return __builtin_bit_cast(f16x4, u32x2{pack2h(p[0], p[1]), pack2h(p[2], p[3])});
+}
+
+template <int G, int NW, int RPW>
+__global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
+    const u16* __restrict__ q_nope, const u16* __restrict__ q_rope,
+    const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
+    int max_ctx, int h_q, int s_q, int chunk, int n_split, int nz, int batch, float scale_log2,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    constexpr int T16 = 16;
+    constexpr int W = 2 * G * DH + DR;
+    constexpr int STRIDE = W + 16;
+    constexpr int NT = NW * 64;
+    constexpr int NLOAD = (T16 * (W / 8) + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) u16 lds[T16 * STRIDE];
+
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int zb = slot % nz;
+    const int unit = (slot / nz) * 8 + xcd;
+    if (unit >= n_split * batch) return;
+    const int p = unit / batch, bb = unit - p * batch;
+    const int b = bb + p % batch < batch ? bb + p % batch : bb + p % batch - batch;
+    const int L = clampi(ctx_lens[b], 0, max_ctx);
+    const int t0 = p * chunk;
+    if (t0 >= L) return;
+    const int t1 = min(t0 + chunk, L);
+    const int ntiles = (t1 - t0 + T16 - 1) / T16;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int q4 = lane >> 4, r16 = lane & 15;
+    const int hpg = h_q / G;
+    const int rows_g = s_q * hpg;
+    const int RT = (rows_g + 15) >> 4;
+    const int wu = zb * NW + wave;
+    const bool active = wu * RPW < G * RT;
+    const int j = active ? (wu * RPW) / RT : 0;
+    const int rt0 = active ? wu * RPW - j * RT : 0;
+    bool row_ok[RPW];
+    int nvis[RPW], qrow[RPW];
+#pragma unroll
+    for (int rg = 0; rg < RPW; ++rg) {
+        const int rho = (rt0 + rg) * 16 + r16;
+        row_ok[rg] = active && rho < rows_g;
+        const int s = row_ok[rg] ? rho / hpg : 0;
+        const int h = j * hpg + (row_ok[rg] ? rho - s * hpg : 0);
+        nvis[rg] = clampi(L - s_q + s + 1, 0, L);
+        qrow[rg] = (b * s_q + s) * h_q + h;
+    }
+
+    f16x8 qv[RPW][6];
+#pragma unroll
+    for (int rg = 0; rg < RPW; ++rg)
+#pragma unroll
+        for (int kk = 0; kk < 6; ++kk) {
+            if (row_ok[rg]) {
+                const u16* src = kk < 4 ? q_nope + (size_t)qrow[rg] * DH + kk * 32 + q4 * 8
+                                        : q_rope + (size_t)qrow[rg] * DR + (kk - 4) * 32 + q4 * 8;
+                qv[rg][kk] = as_f16x8(bf8_to_h8(*reinterpret_cast<const u32x4*>(src)));
+            } else {
+                qv[rg][kk] = zero_f16x8();
+            }
+        }
+
+    floatx4 oacc[RPW][DH / 16];
+#pragma unroll
+    for (int rg = 0; rg < RPW; ++rg)
+#pragma unroll
+        for (int n = 0; n < DH / 16; ++n) oacc[rg][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    SoftmaxState st[RPW];
+#pragma unroll
+    for (int rg = 0; rg < RPW; ++rg) st[rg] = SoftmaxState{kNegInf, 0.f};
+
+    const u16* seq = cache + (size_t)b * bstride;
+    u32x4 reg[NLOAD];
+    load_tile<W, NT, NLOAD, T16>(reg, seq + (size_t)t0 * W, min(T16, t1 - t0), tid);
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int tb = t0 + it * T16;
+        if (it > 0) __syncthreads();
+        store_tile<W, STRIDE, NT, NLOAD, T16>(lds, reg, tid);
+        __syncthreads();
+        if (it + 1 < ntiles) {
+            const int tn = tb + T16;
+            load_tile<W, NT, NLOAD, T16>(reg, seq + (size_t)tn * W, min(T16, t1 - tn), tid);
+        }
+        if (!active) continue;
+
+        f16x4 pb[RPW];
+        {
+            floatx4 acc[RPW][2] = {};
+#pragma unroll
+            for (int kk = 0; kk < 6; ++kk) {
+                const int col = kk < 4 ? j * DH + kk * 32 + q4 * 8 : 2 * G * DH + (kk - 4) * 32 + q4 * 8;
+                const f16x8 a = ld_f16x8(lds + r16 * STRIDE + col);
+#pragma unroll
+                for (int rg = 0; rg < RPW; ++rg) acc[rg][kk & 1] = mfma16h(a, qv[rg][kk], acc[rg][kk & 1]);
+            }
+#pragma unroll
+            for (int rg = 0; rg < RPW; ++rg) {
+                float sc[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tb + q4 * 4 + i;
+                    const float v = acc[rg][0][i] + acc[rg][1][i];
+                    sc[i] = (row_ok[rg] && t < t1 && t < nvis[rg]) ? v * scale_log2 : kNegInf;
+                }
+                bool rescale;
+                float alpha;
+                pb[rg] = softmax_tile4(st[rg], sc, rescale, alpha);
+                if (__builtin_expect(rescale, 0)) {
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int n = 0; n < DH / 16; ++n) oacc[rg][n] *= alpha;
+                }
+            }
+        }
+        // A operand: feature vcol + 16n + r16 at the lane's tokens 4q4 .. 4q4 + 3
+        const u16* vbase = lds + (4 * q4 + (r16 >> 2)) * STRIDE + (G + j) * DH + 4 * (r16 & 3);
+#pragma unroll
+        for (int n = 0; n < DH / 16; ++n) {
+            const f16x4 a = __builtin_bit_cast(f16x4, lds_read_tr16(vbase + 16 * n));
+#pragma unroll
+            for (int rg = 0; rg < RPW; ++rg)
+                oacc[rg][n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb[rg], oacc[rg][n], 0, 0, 0);
+        }
+    }
+
+#pragma unroll
+    for (int rg = 0; rg < RPW; ++rg) {
+        if (!row_ok[rg]) continue;
+        const float l = wave_sum16x4(st[rg].l);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const size_t prow = (size_t)p * batch * s_q * h_q + qrow[rg];
+        float* po = part_o + prow * DH;
+#pragma unroll
+        for (int n = 0; n < DH / 16; ++n) *reinterpret_cast<floatx4*>(po + 16 * n + 4 * q4) = oacc[rg][n] * inv;
+        if (q4 == 0) part_lse[prow] = l > 0.f ? (st[rg].m + __log2f(l)) * kLn2 : kNegInf;
+    }
+}
+
+template <int G, int NW, int RPW>
+hipError_t launch_gqa16_t(const DecodeArgs& a, hipStream_t st) {
+    const int rows_g = a.s_q * (a.h_q / a.g);
+    const int waves = G * ((rows_g + 15) / 16) / RPW;
+    const int nz = (waves + NW - 1) / NW;
+    const int units = a.n_split * a.batch;
+    dim3 grid(((units + 7) / 8) * 8 * nz);
+    hipError_t e = record_if(a.ev_before, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gqa_decode16_kernel<G, NW, RPW>), grid, dim3(NW * 64), 0, st,
+                       (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.cache, a.bstride,
+                       a.ctx_lens, a.max_ctx, a.h_q, a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e,
+                       a.part_o, a.part_lse);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return record_if(a.ev_after, st);
+}
+
 template <int G, int NW, int RPW>
 hipError_t launch_gqa_t(const DecodeArgs& a, hipStream_t st) {
     const int rows_g = a.s_q * (a.h_q / a.g);
@@ -317,13 +506,16 @@ hipError_t launch_gqa_t(const DecodeArgs& a, hipStream_t st) {
 
 // 8 waves per block (with 1024-thread blocks the 128-register cap spills the staging
 // registers).  Two row tiles per wave when a group has an even number of them and one
-// tile per wave would take more than one block, for g <= 4: at g = 8 the 2112-wide
-// tile's staging registers plus two tiles' state exceed 256 (47 spills), so there the
-// second block of pairs re-reads the tiles, through L2 when it keeps pace.
+// tile per wave would take more than one block; at g = 8 that runs on 16-token tiles,
+// since the 32-row 2112-wide tile's staging registers plus two row tiles' state exceed
+// 256 (47 spills).
 template <int G>
 hipError_t launch_gqa_g(const DecodeArgs& a, hipStream_t st) {
     const int rt = (a.s_q * (a.h_q / a.g) + 15) / 16;
-    if (G <= 4 && rt % 2 == 0 && G * rt > 8) return launch_gqa_t<G, 8, 2>(a, st);
+    if (rt % 2 == 0 && G * rt > 8) {
+        if constexpr (G <= 4) return launch_gqa_t<G, 8, 2>(a, st);
+        else return launch_gqa16_t<G, 8, 2>(a, st);
+    }
     return launch_gqa_t<G, 8, 1>(a, st);
 }
 
