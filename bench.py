@@ -336,7 +336,14 @@ def main(argv=None):
 
     rq = cfg.s_q * cfg.h_q
     absorb_name = "absorb_decode_kernel<%d, 1>" % (2 if rq <= 32 else (4 if rq <= 64 else 8))
-    gqa_name = "gqa_decode_kernel<%d, 8>" % cfg.g
+    # the GQA launcher's choice: two row tiles per wave when a group has an even number
+    # of 16-row tiles and one per wave would need more than one workgroup (16-token
+    # tiles at g = 8)
+    rt = (cfg.s_q * (cfg.h_q // cfg.g) + 15) // 16
+    if rt % 2 == 0 and cfg.g * rt > 8:
+        gqa_name = ("gqa_decode_kernel<%d, 8, 2>" % cfg.g) if cfg.g <= 4 else ("gqa_decode16_kernel<%d, 8, 2>" % cfg.g)
+    else:
+        gqa_name = "gqa_decode_kernel<%d, 8, 1>" % cfg.g
     paths = {"absorb": path_rec(work_a, call_a, kern_a, split_a, absorb_name),
              "gqa": path_rec(work_g, call_g, kern_g, split_g, gqa_name)}
 
