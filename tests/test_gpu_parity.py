@@ -149,17 +149,19 @@ def test_chunk_boundary_causal(gqla):
     both_paths(cfg, [97, 65], gqla, 2, max_ctx=129, what="causal-boundary")
 
 
-def test_rising_scores(gqla):
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_rising_scores(gqla, s_q):
     """Latent rows whose scale grows along the sequence, so the softmax maximum rises by
     more than the online softmax's slack (10 log2 units) after rows have accumulated:
     the kernels must raise their reference and rescale what they hold (a ramp on
     sequence 0, a sudden jump on sequence 1; a replay of the lazy-reference rule on the
     CPU counts 24 and 57 such raises over the heads).  The peak logits stay near 10:
     the absorb path rounds its absorbed query to fp16, an error that grows with |score|,
-    and far sharper softmaxes amplify it past the tolerance."""
+    and far sharper softmaxes amplify it past the tolerance.  At s_q = 2 the GQA path
+    runs its 16-token kernel (two row tiles per wave) and the absorb path two row blocks."""
     import oracle
     torch = gu.torch_mod()
-    cfg = synth.config(3).with_(batch=2)
+    cfg = synth.config(3, s_q=s_q).with_(batch=2)
     lens = [1000, 700]
     w = gu.workload(cfg, lens=lens)
     qn, qr = synth.queries(cfg)
