@@ -38,7 +38,7 @@ constexpr int XTOK_BLOCK = 2048;        // tokens per block (32 tiles)
 template <int G>
 __global__ __launch_bounds__(512) void expand_kernel(
     const u16* __restrict__ latent, int64_t lbs, const u16* __restrict__ w_uk, const u16* __restrict__ w_uv,
-    const int32_t* __restrict__ ctx_lens, int max_ctx, int row_begin, int chunks_per_seq, int n_chunks,
+    const int32_t* __restrict__ ctx_lens, int max_ctx, int row_begin, int batch, int n_chunks,
     u16* __restrict__ gc, int64_t gbs) {
     constexpr int WOUT = 2 * G * DH + DR;
     constexpr int WIN = RK + DR;
@@ -50,9 +50,13 @@ __global__ __launch_bounds__(512) void expand_kernel(
     const int cb = slot % NCB;
     const int chunk = (slot / NCB) * 8 + xcd;
     if (chunk >= n_chunks) return;
-    const int b = chunk / chunks_per_seq;
+    // Chunk-major numbering with the sequence rotated by the chunk index: chunk c of
+    // sequence b lands on XCD (b - c) mod 8 (batch a multiple of 8), so ragged lengths,
+    // whose late chunks are mostly empty, still spread their work over every XCD.
+    const int c = chunk / batch, bb = chunk - c * batch;
+    const int b = bb + c % batch < batch ? bb + c % batch : bb + c % batch - batch;
     const int L = clampi(ctx_lens[b], 0, max_ctx);
-    const int tbeg = row_begin + (chunk - b * chunks_per_seq) * XTOK_BLOCK;
+    const int tbeg = row_begin + c * XTOK_BLOCK;
     if (tbeg >= L) return;
     const int tend = min(tbeg + XTOK_BLOCK, L);
 
@@ -228,7 +232,7 @@ hipError_t launch_expand_g(const ExpandArgs& a, hipStream_t st) {
     const int n_chunks = cps * a.batch;
     dim3 grid(((n_chunks + 7) / 8) * 8 * (2 * G * DH / XCOLS));
     hipLaunchKernelGGL(expand_kernel<G>, grid, dim3(512), 0, st, (const u16*)a.latent, a.latent_bstride,
-                       (const u16*)a.w_uk, (const u16*)a.w_uv, a.ctx_lens, a.max_ctx, a.row_begin, cps, n_chunks,
+                       (const u16*)a.w_uk, (const u16*)a.w_uv, a.ctx_lens, a.max_ctx, a.row_begin, a.batch, n_chunks,
                        (u16*)a.group_cache, a.group_bstride);
     return hipGetLastError();
 }
