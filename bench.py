@@ -84,8 +84,10 @@ def sources_digest(paths):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_key, digest):
-    """Counter-derived HBM bytes per launch from profiles/traffic.json, if taken on this source."""
+def load_traffic(kernel_key, digest, workload):
+    """Counter-derived HBM bytes per launch from profiles/traffic.json, if taken on this
+    source and this workload (the records are of the flagship workload unless they name
+    another)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -93,7 +95,7 @@ def load_traffic(kernel_key, digest):
         rec = json.load(open(path)).get(kernel_key)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_digest") != digest:
+    if not rec or rec.get("source_digest") != digest or rec.get("workload", "flagship") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -269,16 +271,20 @@ def main(argv=None):
 
     out_a = torch.empty((B, cfg.s_q, cfg.h_q, cfg.d_h), dtype=torch.bfloat16, device=dev)
     out_g = torch.empty_like(out_a)
-    ws_a = gqla.alloc_workspace(sh, gqla.ABSORB, B, S, 0, dev)
-    ws_g = gqla.alloc_workspace(sh, gqla.GQA, B, S, 0, dev)
-    split_a = gqla.plan_splits(sh, gqla.ABSORB, B, S, 0)
-    split_g = gqla.plan_splits(sh, gqla.GQA, B, S, 0)
+    # split-K partition planned from the context lengths, which the host holds here
+    ns_a = gqla.plan_splits_lens(sh, gqla.ABSORB, w.lens, S)[0]
+    ns_g = gqla.plan_splits_lens(sh, gqla.GQA, w.lens, S)[0]
+    ws_a = gqla.alloc_workspace(sh, gqla.ABSORB, B, S, ns_a, dev)
+    ws_g = gqla.alloc_workspace(sh, gqla.GQA, B, S, ns_g, dev)
+    split_a = gqla.plan_splits(sh, gqla.ABSORB, B, S, ns_a)
+    split_g = gqla.plan_splits(sh, gqla.GQA, B, S, ns_g)
 
     def absorb():
-        gqla.decode_absorb(sh, w.q_nope, w.q_rope, w.w_uk, w.w_uv, w.latent, w.ctx_lens, out_a, None, ws_a)
+        gqla.decode_absorb(sh, w.q_nope, w.q_rope, w.w_uk, w.w_uv, w.latent, w.ctx_lens, out_a, None, ws_a,
+                           num_splits=ns_a)
 
     def gqa():
-        gqla.decode_gqa(sh, w.q_nope, w.q_rope, gc, w.ctx_lens, out_g, None, ws_g)
+        gqla.decode_gqa(sh, w.q_nope, w.q_rope, gc, w.ctx_lens, out_g, None, ws_g, num_splits=ns_g)
 
     note("warm-up")
     for _ in range(args.warmup):
@@ -356,14 +362,14 @@ def main(argv=None):
                + q_tokens * cfg.h_q * (cfg.d_h + cfg.d_r + cfg.d_h) * 2)
         achieved = alg / (kern_g * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("gqa_decode", digest_g),
+                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("gqa_decode", digest_g, args.workload),
                 "kernel": gqa_name, "alg_bytes_per_launch": alg, "avg_ms": round(kern_g, 4)}
     else:
         alg = (rf.absorb_bytes_per_token(cfg.r_kv, cfg.d_r) * total_ctx
                + q_tokens * cfg.h_q * (cfg.r_kv + cfg.d_r + cfg.d_h) * 2 + cfg.g * cfg.d_h * cfg.r_kv * 2)
         achieved = alg / (kern_a * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("absorb_decode", digest_a),
+                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("absorb_decode", digest_a, args.workload),
                 "kernel": absorb_name, "alg_bytes_per_launch": alg, "avg_ms": round(kern_a, 4)}
 
     note("CPU oracle baseline" if not args.no_cpu_baseline else "done timing")

@@ -84,6 +84,26 @@ gqla_status gqla_plan_splits(const gqla_shape* shape, int32_t path, int32_t batc
                              int32_t max_ctx, int32_t num_splits,
                              int32_t* n_split, int32_t* chunk);
 
+/* Split-K planning from context lengths the caller holds on the host (a serving
+ * scheduler usually does), for when the automatic rule, which sees only max_ctx,
+ * leaves compute units idle or runs a second, mostly empty round of chunks: few long
+ * ragged sequences, for instance.  The pages do not describe the split-K partition
+ * (it is this library's way of spreading one sequence's context over compute units);
+ * this call only chooses how finely the decode calls cut it.
+ *   host_ctx_lens [batch] host memory, read only (values clamped to [0, max_ctx]).
+ * Writes *num_splits, the value to pass as num_splits to gqla_workspace_size and the
+ * decode call of the same shape, path, batch and max_ctx, and the *n_split and
+ * *chunk that call then uses.  bf16 absorb and GQA paths: when the automatic plan
+ * needs fewer than four rounds of workgroups on the device, the automatic plan and the
+ * plans whose grid is exactly 1-4 rounds are compared by the estimate
+ * rounds x (chunk + a fixed per-workgroup overhead), and a plan with more chunks wins
+ * only when it is estimated 10 % faster; otherwise, and for other paths and dtypes, the
+ * automatic plan (*num_splits = 0).  Host-only, O(batch).  Errors:
+ * GQLA_ERR_INVALID_ARG on null pointers or invalid shape or sizes. */
+gqla_status gqla_plan_splits_lens(const gqla_shape* shape, int32_t path, int32_t batch,
+                                  int32_t max_ctx, const int32_t* host_ctx_lens,
+                                  int32_t* num_splits, int32_t* n_split, int32_t* chunk);
+
 /* Expand latent rows once into g groups of K and V (section 2, GQA path: the
  * latent is expanded into g K/V groups so decode need not re-expand it each step).
  *   latent      [batch][latent_bstride] elements; sequence b's row t starts at

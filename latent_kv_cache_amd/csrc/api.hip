@@ -124,6 +124,38 @@ Plan plan(const gqla_shape& s, int path, int batch, int max_ctx, int num_splits)
     return p;
 }
 
+// Length-aware choice of num_splits (bf16 absorb and GQA paths).  A decode launch is
+// a grid of workgroups, one per (context chunk, sequence) pair and, on the absorb
+// path, per 128-row group of query rows.  Workgroups of pairs past a sequence's end
+// return at once.  The candidates are the automatic plan and the "fill" plans whose
+// grid is exactly k times the concurrent workgroups of the device (k = 1..4), so that
+// no round of workgroups is partly filled; the estimate of a plan is
+//   rounds x (min(chunk, longest context) + overhead),
+// rounds = ceil(non-empty workgroups / concurrent workgroups), with the per-workgroup
+// overhead (query staging, the W_UV epilogue or output write, the partial it adds to
+// the combine) in tokens: about 1000, fitted on MI355X to the absorb kernel on the
+// ragged 64K-128K workload and kept for the GQA kernel, whose time there also falls
+// with fewer, longer chunks (16 chunks 1082 us, 64 chunks 1166 us).  A plan with more chunks
+// replaces the current choice only when it is estimated 10 % faster: the estimate
+// leaves out costs that grow with the chunk count (dispatch imbalance inside a round,
+// the combine's reads), and a smaller grid also needs less workspace.  Partly filled rounds are
+// estimated as full because the dispatcher places workgroups statically (workgroup i
+// runs on XCD i mod 8, and within an XCD by a fixed rotation), so one crowded group of
+// CUs sets the time: measured at 16 sequences of 64K-128K tokens, 18-22 chunks per
+// sequence (288-352 workgroups for 256 CUs, a quarter of them empty) ran 30-60 %
+// slower than 16 chunks (256 workgroups).
+double split_estimate(const int32_t* lens, int batch, int max_ctx, int chunk, int mult, int slots, double ovh) {
+    long long units = 0;
+    int longest = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int L = std::min(std::max(lens[b], 0), max_ctx);
+        units += (long long)mult * ((L + chunk - 1) / chunk);
+        longest = std::max(longest, L);
+    }
+    const long long rounds = (units + slots - 1) / slots;
+    return (double)rounds * (std::min(chunk, longest) + ovh);
+}
+
 struct Layout {
     size_t part_o, part_lse, qhat, total;
 };
@@ -260,6 +292,68 @@ gqla_status gqla_plan_splits(const gqla_shape* shape, int32_t path, int32_t batc
     if (num_splits < 0) return fail(GQLA_ERR_INVALID_ARG, "num_splits=%d < 0", num_splits);
     if (!n_split || !chunk) return fail(GQLA_ERR_INVALID_ARG, "n_split or chunk is null");
     const Plan p = plan(*shape, path, batch, max_ctx, num_splits);
+    *n_split = p.n_split;
+    *chunk = p.chunk;
+    return ok();
+}
+
+gqla_status gqla_plan_splits_lens(const gqla_shape* shape, int32_t path, int32_t batch, int32_t max_ctx,
+                                  const int32_t* host_ctx_lens, int32_t* num_splits, int32_t* n_split,
+                                  int32_t* chunk) {
+    TRY(check_shape(shape, path));
+    TRY(check_sizes(batch, max_ctx));
+    if (!host_ctx_lens && batch > 0) return fail(GQLA_ERR_INVALID_ARG, "host_ctx_lens is null");
+    if (!num_splits || !n_split || !chunk) return fail(GQLA_ERR_INVALID_ARG, "num_splits, n_split or chunk is null");
+    const gqla_shape& s = *shape;
+    int best = 0;
+    if (s.dtype == GQLA_BF16 && (path == GQLA_PATH_ABSORB || path == GQLA_PATH_GQA) && batch > 0 && max_ctx > 0) {
+        int mult = 1, per_cu = 1;
+        const double ovh = 1000.0;
+        if (path == GQLA_PATH_ABSORB) {
+            const int rows = gqla::absorb_block_rows(s.s_q * s.h_q);
+            mult = (s.s_q * s.h_q + rows - 1) / rows;
+        } else {
+            const size_t tile = (size_t)gqla::kBf16TokenTile * (2 * s.g * s.d_h + s.d_r) * 2;
+            if (tile < (64u << 10)) per_cu = std::min(4, (int)(((140u << 10) + tile - 1) / tile));
+        }
+        const int slots = device_cus() * per_cu;
+        const int auto_chunk = plan(s, path, batch, max_ctx, 0).chunk;
+        long long auto_units = 0;
+        for (int b = 0; b < batch; ++b)
+            auto_units += (long long)mult * ((std::min(std::max(host_ctx_lens[b], 0), max_ctx) + auto_chunk - 1) / auto_chunk);
+        // with four or more rounds of workgroups, partial rounds and short last chunks are
+        // a small share of the time and the automatic plan stands
+        if (auto_units < 4LL * slots) {
+            // candidates (num_splits argument, chunks per sequence), fewest chunks first
+            int cand_w[5], cand_n[5], nc = 0;
+            const int fill = slots / (batch * mult);   // chunks per sequence, one round
+            for (int k = 1; fill > 0 && k <= 4; ++k) {
+                const Plan pl = plan(s, path, batch, max_ctx, k * fill);
+                if (pl.n_split * batch * mult > k * slots) continue;   // chunk alignment overflowed the grid
+                cand_w[nc] = k * fill;
+                cand_n[nc++] = pl.n_split;
+            }
+            cand_w[nc] = 0;
+            cand_n[nc++] = plan(s, path, batch, max_ctx, 0).n_split;
+            for (int i = 1; i < nc; ++i)
+                for (int j = i; j > 0 && cand_n[j] < cand_n[j - 1]; --j) {
+                    std::swap(cand_n[j], cand_n[j - 1]);
+                    std::swap(cand_w[j], cand_w[j - 1]);
+                }
+            double best_est = 0.0;
+            for (int i = 0; i < nc; ++i) {
+                const double est =
+                    split_estimate(host_ctx_lens, batch, max_ctx, plan(s, path, batch, max_ctx, cand_w[i]).chunk, mult,
+                                   slots, ovh);
+                if (i == 0 || est < best_est * 0.9) {
+                    best = cand_w[i];
+                    best_est = est;
+                }
+            }
+        }
+    }
+    const Plan p = plan(s, path, batch, max_ctx, best);
+    *num_splits = best;
     *n_split = p.n_split;
     *chunk = p.chunk;
     return ok();

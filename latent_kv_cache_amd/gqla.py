@@ -23,7 +23,7 @@ BF16, F32 = 0, 1
 ABSORB, GQA, SPARSE = 0, 1, 2
 STATUS = {0: "GQLA_OK", 1: "GQLA_ERR_INVALID_ARG", 2: "GQLA_ERR_UNSUPPORTED", 3: "GQLA_ERR_WORKSPACE", 4: "GQLA_ERR_HIP"}
 
-EXPORTS = ("gqla_workspace_size", "gqla_plan_splits", "gqla_expand_groups", "gqla_decode_absorb",
+EXPORTS = ("gqla_workspace_size", "gqla_plan_splits", "gqla_plan_splits_lens", "gqla_expand_groups", "gqla_decode_absorb",
            "gqla_decode_gqa", "gqla_decode_gqa_sparse", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
            "gqla_set_kernel_events", "gqla_status_string", "gqla_last_error")
 
@@ -68,6 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sp = ctypes.POINTER(Shape)
     lib.gqla_workspace_size.argtypes = [sp, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]
     lib.gqla_plan_splits.argtypes = [sp, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
+    lib.gqla_plan_splits_lens.argtypes = [sp, c_i32, c_i32, c_i32, c_vp, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32),
+                                          ctypes.POINTER(c_i32)]
     lib.gqla_expand_groups.argtypes = [sp, c_i32, c_i32, c_vp, c_i64, c_vp, c_vp, c_vp, c_i32, c_vp, c_i64, c_vp]
     lib.gqla_decode_absorb.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp,
                                        c_vp, c_sz, c_i32, c_vp]
@@ -81,7 +83,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqla_measure_peaks.argtypes = [c_vp, c_sz, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                        c_vp]
     lib.gqla_set_kernel_events.argtypes = [c_vp, c_vp]
-    for name in ("gqla_workspace_size", "gqla_plan_splits", "gqla_expand_groups", "gqla_decode_absorb",
+    for name in ("gqla_workspace_size", "gqla_plan_splits", "gqla_plan_splits_lens", "gqla_expand_groups", "gqla_decode_absorb",
                  "gqla_decode_gqa", "gqla_decode_gqa_sparse", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
                  "gqla_set_kernel_events"):
         getattr(lib, name).restype = ctypes.c_int
@@ -126,6 +128,18 @@ def plan_splits(shape: Shape, path: int, batch: int, max_ctx: int, num_splits: i
     _check(load().gqla_plan_splits(ctypes.byref(shape), path, batch, max_ctx, num_splits, ctypes.byref(n),
                                    ctypes.byref(c)))
     return int(n.value), int(c.value)
+
+
+def plan_splits_lens(shape: Shape, path: int, ctx_lens, max_ctx: int) -> Tuple[int, int, int]:
+    """gqla_plan_splits_lens over host context lengths (any int sequence or array):
+    returns (num_splits to pass to the decode call, n_split, chunk)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(ctx_lens, dtype=np.int32))
+    w, n, c = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    ptr = lens.ctypes.data if lens.size else None
+    _check(load().gqla_plan_splits_lens(ctypes.byref(shape), path, int(lens.size), max_ctx, ptr, ctypes.byref(w),
+                                        ctypes.byref(n), ctypes.byref(c)))
+    return int(w.value), int(n.value), int(c.value)
 
 
 def set_kernel_events(before=None, after=None) -> None:

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from latent_kv_cache_amd import gqla
@@ -219,3 +220,39 @@ def test_sparse_argument_validation(lib):
 def test_binding_raises_without_status_ok(lib):
     with pytest.raises(gqla.GQLAError):
         gqla.workspace_size(gqla.make_shape(128, 7, 512, 64, 128, 1), gqla.GQA, 1, 1)
+
+
+def test_plan_lens_long_ragged_context(lib):
+    # 16 sequences of 64K-128K tokens: the automatic rule (chunks <= 4096 tokens) makes
+    # about 388 (chunk, sequence) units, a second round on 256 compute units; planned
+    # from the lengths, every unit fits in one round and the count is a valid num_splits
+    rng = np.random.default_rng(5)
+    lens = rng.integers(65536, 131073, size=16).astype(np.int32)
+    cap = int(lens.max())
+    for path in (gqla.ABSORB, gqla.GQA):
+        w, n, c = gqla.plan_splits_lens(FLAG, path, lens, cap)
+        assert w > 0 and (n, c) == gqla.plan_splits(FLAG, path, 16, cap, w)
+        units = sum((int(L) + c - 1) // c for L in lens)
+        assert units <= 256 and n * c >= cap
+        assert c > gqla.plan_splits(FLAG, path, 16, cap, 0)[1]
+
+
+def test_plan_lens_uniform_flagship(lib):
+    # 128 sequences of 8192 tokens on 256 compute units: two chunks each, one per CU
+    lens = np.full(128, 8192, dtype=np.int32)
+    for path in (gqla.ABSORB, gqla.GQA):
+        w, n, c = gqla.plan_splits_lens(FLAG, path, lens, 8192)
+        assert (n, c) == (2, 4096)
+
+
+def test_plan_lens_edges(lib):
+    # empty batch, zero and clamped lengths, fp32 (automatic plan), null lengths
+    assert gqla.plan_splits_lens(FLAG, gqla.ABSORB, [], 8192)[0] == 0
+    w, n, c = gqla.plan_splits_lens(FLAG, gqla.GQA, [0, 0, 100000], 4096)
+    assert n * c >= 4096 and c % 32 == 0
+    sh = gqla.make_shape(16, 2, 64, 16, 32, 1, dtype=gqla.F32)
+    assert gqla.plan_splits_lens(sh, gqla.ABSORB, [300], 300)[0] == 0
+    w, n, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = lib.gqla_plan_splits_lens(ctypes.byref(FLAG), gqla.GQA, 2, 64, None, ctypes.byref(w), ctypes.byref(n),
+                                   ctypes.byref(c))
+    assert st == 1
