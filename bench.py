@@ -341,7 +341,7 @@ def main(argv=None):
                 "n_split": splits[0], "chunk": splits[1]}
 
     rq = cfg.s_q * cfg.h_q
-    absorb_name = "absorb_decode_kernel<%d, 1>" % (2 if rq <= 32 else (4 if rq <= 64 else 8))
+    absorb_name = "absorb_decode_kernel<8, 1, %d>" % (4 if rq <= 32 else (2 if rq <= 64 else 1))
     # the GQA launcher's choice: two row tiles per wave when a group has an even number
     # of 16-row tiles and one per wave would need more than one workgroup (16-token
     # tiles at g = 8)

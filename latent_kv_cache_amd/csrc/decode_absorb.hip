@@ -247,7 +247,7 @@ __device__ __forceinline__ void block_sync() {
     asm volatile("" ::: "memory");
 }
 
-template <int NW, int RG>
+template <int NW, int RG, int CS>
 __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     const u16* __restrict__ qhat, const u16* __restrict__ w_uv,
     const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
@@ -263,11 +263,13 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     constexpr int TSLOTS = TT * SROW;              // slots of a tile
     constexpr int NDMA = (TSLOTS + NT - 1) / NT;   // direct loads per wave per tile
     constexpr int BSLOTS = NDMA * NT;              // slots of a buffer (spare tail included)
-    constexpr int BROWS = NW * 16 * RG;            // query rows of a workgroup
+    constexpr int BROWS = (NW / CS) * 16 * RG;     // query rows of a workgroup
+    constexpr int NUW = NU / CS;                   // column tiles of U^T per wave
+    static_assert(NW % CS == 0 && NU % CS == 0 && (CS == 1 || RG == 1), "column split");
     constexpr int QRS = DR + 16;                   // LDS row stride of the rotary queries
     // column tile of the U loop at which conversion slot i is read, and written back
-    constexpr auto cv_read = [](int i) { return i * NU / NDMA; };
-    constexpr auto cv_write = [](int i) { return i * NU / NDMA + 2 < NU ? i * NU / NDMA + 2 : NU - 1; };
+    constexpr auto cv_read = [](int i) { return i * NUW / NDMA; };
+    constexpr auto cv_write = [](int i) { return i * NUW / NDMA + 2 < NUW ? i * NUW / NDMA + 2 : NUW - 1; };
     // three separately declared buffers: with the tile loop unrolled by three every
     // access names a fixed buffer, so the compiler can tell that reading one buffer
     // does not depend on the direct loads still landing in the others
@@ -299,7 +301,9 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     const int q4 = lane >> 4, r16 = lane & 15;
     const int RQ = s_q * h_q;
     const int hpg = h_q / g;
-    const int rho0 = z * BROWS + wave * (16 * RG);  // first row of the wave
+    // wave = wslot * CS + part: row slot wslot, latent column part `part` of u
+    const int wslot = wave / CS, part = wave - (wave / CS) * CS;
+    const int rho0 = z * BROWS + wslot * (16 * RG);  // first row of the wave
     const bool active = rho0 < RQ;
     int nvis[RG];
     bool row_ok[RG];
@@ -353,11 +357,11 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
         *reinterpret_cast<u32x4*>(qr_lds + r * QRS + col * 8) = v;
     }
 
-    floatx4 uacc[RG][NU];
+    floatx4 uacc[RG][NUW];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int n = 0; n < NU; ++n) uacc[rg][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < NUW; ++n) uacc[rg][n] = floatx4{0.f, 0.f, 0.f, 0.f};
     SoftmaxState st[RG];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) st[rg] = SoftmaxState{kNegInf, 0.f};
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
                     const f16x8 bq = kk < KL ? qv[rg][kk]
-                                             : ld_f16x8(qr_lds + (wave * 16 * RG + 16 * rg + r16) * QRS +
+                                             : ld_f16x8(qr_lds + (wslot * 16 * RG + 16 * rg + r16) * QRS +
                                                         (kk - KL) * 32 + q4 * 8);
                     acc[rg][0] = mfma16h(a0, bq, acc[rg][0]);
                     acc[rg][1] = mfma16h(a1, bq, acc[rg][1]);
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
                     // the common path
                     asm volatile("" ::: "memory");
 #pragma unroll
-                    for (int n = 0; n < NU; ++n) uacc[rg][n] *= alpha;
+                    for (int n = 0; n < NUW; ++n) uacc[rg][n] *= alpha;
                 }
             }
         }
@@ -428,12 +432,12 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
         // column tiles later, so only a few slots are held in registers at a time
         u32x4 cv[NDMA];
 #pragma unroll
-        for (int n = 0; n < NU; ++n) {
+        for (int n = 0; n < NUW; ++n) {
 #pragma unroll
             for (int i = 0; i < NDMA; ++i)
                 if (cv_read(i) == n)
                     cv[i] = *reinterpret_cast<const u32x4*>(next_lds + ((i * NW + wave) * 64 + lane) * 8);
-            const f16x8 a = gather_col(lds, STRIDE, q4, r16, 16 * n);
+            const f16x8 a = gather_col(lds, STRIDE, q4, r16, 16 * (part * NUW + n));
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) uacc[rg][n] = mfma16h(a, pb[rg], uacc[rg][n]);
 #pragma unroll
@@ -462,65 +466,142 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     }
     // no direct load may still be writing this workgroup's LDS when it ends
     wait_vmcnt<0>();
-    if (!active) return;
+    if constexpr (CS == 1) {
+        if (!active) return;
 
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        const int rho = rho0 + 16 * rg + r16;
-        const int s = row_ok[rg] ? rho / h_q : 0;
-        const int h = row_ok[rg] ? rho - s * h_q : 0;
-        const float l = wave_sum16x4(st[rg].l);
+    #pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            const int rho = rho0 + 16 * rg + r16;
+            const int s = row_ok[rg] ? rho / h_q : 0;
+            const int h = row_ok[rg] ? rho - s * h_q : 0;
+            const float l = wave_sum16x4(st[rg].l);
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            // U^T as the B operand of o^T = W_UV[j] U^T: k-step ks covers latent columns
+            // 32ks + (token slot order of P), which are uacc[2ks + e/4][e%4] of this lane
+            bf16x8 ub[RK / 32], ul[RK / 32];
+    #pragma unroll
+            for (int ks = 0; ks < RK / 32; ++ks) {
+                u32x4 vh, vl;
+    #pragma unroll
+                for (int hh = 0; hh < 4; ++hh) {
+                    const floatx4& src = uacc[rg][2 * ks + (hh >> 1)];
+                    const float a = src[2 * (hh & 1)] * inv, c = src[2 * (hh & 1) + 1] * inv;
+                    const u16 ah = f2bf(a), ch = f2bf(c);
+                    vh[hh] = pack2(ah, ch);
+                    vl[hh] = pack2f(a - bf2f(ah), c - bf2f(ch));
+                }
+                ub[ks] = as_bf16x8(vh);
+                ul[ks] = as_bf16x8(vl);
+            }
+            const int jrow = h / hpg;
+            const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
+            // groups of the row group's 16 rows (they never straddle a query token: h_q % 16 == 0)
+            const int first = rho0 + 16 * rg;
+            const int last = min(first + 15, RQ - 1);
+            if (first > last) continue;
+            const int jlo = (first % h_q) / hpg, jhi = (last % h_q) / hpg;
+            for (int jj = jlo; jj <= jhi; ++jj) {
+                const u16* wj = w_uv + (size_t)jj * DH * RK;
+    #pragma unroll 2
+                for (int mt = 0; mt < DH / 16; ++mt) {
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                    const u16* wrow = wj + (size_t)(mt * 16 + r16) * RK + q4 * 4;
+    #pragma unroll
+                    for (int ks = 0; ks < RK / 32; ++ks) {
+                        const u32x2 lo = *reinterpret_cast<const u32x2*>(wrow + ks * 32);
+                        const u32x2 hi = *reinterpret_cast<const u32x2*>(wrow + ks * 32 + 16);
+                        const bf16x8 wa = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                        acc = mfma16(wa, ub[ks], acc);
+                        acc = mfma16(wa, ul[ks], acc);
+                    }
+                    if (row_ok[rg] && jrow == jj) *reinterpret_cast<floatx4*>(part_o + prow * DH + mt * 16 + q4 * 4) = acc;
+                }
+            }
+            if (row_ok[rg] && q4 == 0) part_lse[prow] = l > 0.f ? (st[rg].m + __log2f(l)) * kLn2 : kNegInf;
+        }
+    } else {
+        // Column-split epilogue (one row group per wave).  The wave holds u for its 16 rows
+        // over latent columns [part * RK / CS, (part + 1) * RK / CS), so its W_UV product
+        // is a partial sum over those columns; the CS partials of a row slot meet in LDS
+        // (the tile buffers, free once every wave has passed the barrier below) and each
+        // wave of the slot sums and writes every CS-th 16-wide block of d_h.
+        block_sync();
+        constexpr int KSW = NUW / 2;   // k-steps of the wave's columns
+        const int rho = rho0 + r16;
+        const bool rok = row_ok[0];
+        const int s = rok ? rho / h_q : 0;
+        const int h = rok ? rho - s * h_q : 0;
+        const float l = wave_sum16x4(st[0].l);
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        // U^T as the B operand of o^T = W_UV[j] U^T: k-step ks covers latent columns
-        // 32ks + (token slot order of P), which are uacc[2ks + e/4][e%4] of this lane
-        bf16x8 ub[RK / 32], ul[RK / 32];
+        bf16x8 ub[KSW], ul[KSW];
 #pragma unroll
-        for (int ks = 0; ks < RK / 32; ++ks) {
+        for (int ks = 0; ks < KSW; ++ks) {
             u32x4 vh, vl;
 #pragma unroll
             for (int hh = 0; hh < 4; ++hh) {
-                const floatx4& src = uacc[rg][2 * ks + (hh >> 1)];
-                const float a = src[2 * (hh & 1)] * inv, c = src[2 * (hh & 1) + 1] * inv;
-                const u16 ah = f2bf(a), ch = f2bf(c);
-                vh[hh] = pack2(ah, ch);
-                vl[hh] = pack2f(a - bf2f(ah), c - bf2f(ch));
+                const floatx4& src = uacc[0][2 * ks + (hh >> 1)];
+                const float x = src[2 * (hh & 1)] * inv, y = src[2 * (hh & 1) + 1] * inv;
+                const u16 xh = f2bf(x), yh = f2bf(y);
+                vh[hh] = pack2(xh, yh);
+                vl[hh] = pack2f(x - bf2f(xh), y - bf2f(yh));
             }
             ub[ks] = as_bf16x8(vh);
             ul[ks] = as_bf16x8(vl);
         }
         const int jrow = h / hpg;
-        const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
-        // groups of the row group's 16 rows (they never straddle a query token: h_q % 16 == 0)
-        const int first = rho0 + 16 * rg;
-        const int last = min(first + 15, RQ - 1);
-        if (first > last) continue;
-        const int jlo = (first % h_q) / hpg, jhi = (last % h_q) / hpg;
-        for (int jj = jlo; jj <= jhi; ++jj) {
-            const u16* wj = w_uv + (size_t)jj * DH * RK;
-#pragma unroll 2
-            for (int mt = 0; mt < DH / 16; ++mt) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                const u16* wrow = wj + (size_t)(mt * 16 + r16) * RK + q4 * 4;
+        floatx4 ores[DH / 16];
 #pragma unroll
-                for (int ks = 0; ks < RK / 32; ++ks) {
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(wrow + ks * 32);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(wrow + ks * 32 + 16);
-                    const bf16x8 wa = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-                    acc = mfma16(wa, ub[ks], acc);
-                    acc = mfma16(wa, ul[ks], acc);
+        for (int mt = 0; mt < DH / 16; ++mt) ores[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (active) {
+            const int first = rho0;
+            const int last = min(first + 15, RQ - 1);
+            const int jlo = (first % h_q) / hpg, jhi = (last % h_q) / hpg;
+            for (int jj = jlo; jj <= jhi; ++jj) {
+                const u16* wj = w_uv + (size_t)jj * DH * RK + part * (RK / CS);
+#pragma unroll
+                for (int mt = 0; mt < DH / 16; ++mt) {
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                    const u16* wrow = wj + (size_t)(mt * 16 + r16) * RK + q4 * 4;
+#pragma unroll
+                    for (int ks = 0; ks < KSW; ++ks) {
+                        const u32x2 lo = *reinterpret_cast<const u32x2*>(wrow + ks * 32);
+                        const u32x2 hi = *reinterpret_cast<const u32x2*>(wrow + ks * 32 + 16);
+                        const bf16x8 wa = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                        acc = mfma16(wa, ub[ks], acc);
+                        acc = mfma16(wa, ul[ks], acc);
+                    }
+                    if (jrow == jj) ores[mt] = acc;
                 }
-                if (row_ok[rg] && jrow == jj) *reinterpret_cast<floatx4*>(part_o + prow * DH + mt * 16 + q4 * 4) = acc;
             }
         }
-        if (row_ok[rg] && q4 == 0) part_lse[prow] = l > 0.f ? (st[rg].m + __log2f(l)) * kLn2 : kNegInf;
+        // partial of wave w, block mt: buffer mt / 4, floatx4 slot (w * 4 + mt % 4) * 64 + lane
+        float* red0 = reinterpret_cast<float*>(buf0);
+        float* red1 = reinterpret_cast<float*>(buf1);
+        static_assert(NW * 4 * 64 * 16 <= (int)sizeof(buf0), "partials fit in a tile buffer");
+#pragma unroll
+        for (int mt = 0; mt < DH / 16; ++mt)
+            *reinterpret_cast<floatx4*>((mt < 4 ? red0 : red1) + ((wave * 4 + (mt & 3)) * 64 + lane) * 4) = ores[mt];
+        block_sync();
+        if (active && rok) {
+            const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
+            for (int mt = part; mt < DH / 16; mt += CS) {
+                floatx4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < CS; ++c)
+                    sum += *reinterpret_cast<const floatx4*>((mt < 4 ? red0 : red1) +
+                                                             (((wslot * CS + c) * 4 + (mt & 3)) * 64 + lane) * 4);
+                *reinterpret_cast<floatx4*>(part_o + prow * DH + mt * 16 + q4 * 4) = sum;
+            }
+            if (part == 0 && q4 == 0) part_lse[prow] = l > 0.f ? (st[0].m + __log2f(l)) * kLn2 : kNegInf;
+        }
     }
 }
 
-template <int NW, int RG>
+template <int NW, int RG, int CS>
 hipError_t launch_absorb_t(const DecodeArgs& a, int nz, hipStream_t st) {
     const int pairs = a.n_split * a.batch;
     dim3 grid(((pairs + 7) / 8) * 8 * nz);
-    hipLaunchKernelGGL((absorb_decode_kernel<NW, RG>), grid, dim3(NW * 64), 0, st, (const u16*)a.qhat,
+    hipLaunchKernelGGL((absorb_decode_kernel<NW, RG, CS>), grid, dim3(NW * 64), 0, st, (const u16*)a.qhat,
                        (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens, a.max_ctx, a.h_q, a.g,
                        a.s_q, a.chunk, a.n_split, nz, a.batch, a.part_o, a.part_lse);
     return hipGetLastError();
@@ -545,11 +626,11 @@ hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st) {
     e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;
     if (rows == 32) {
-        e = launch_absorb_t<2, 1>(a, nz, st);
+        e = launch_absorb_t<8, 1, 4>(a, nz, st);
     } else if (rows == 64) {
-        e = launch_absorb_t<4, 1>(a, nz, st);
+        e = launch_absorb_t<8, 1, 2>(a, nz, st);
     } else {
-        e = launch_absorb_t<8, 1>(a, nz, st);
+        e = launch_absorb_t<8, 1, 1>(a, nz, st);
     }
     if (e != hipSuccess) return e;
     return record_if(a.ev_after, st);
