@@ -21,7 +21,6 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -68,36 +67,6 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
-# sources whose digest a counter record in profiles/traffic.json must match
-KERNEL_SOURCES = {
-    "gqa_decode": ["latent_kv_cache_amd/csrc/decode_gqa.hip", "latent_kv_cache_amd/csrc/common.h"],
-    "absorb_decode": ["latent_kv_cache_amd/csrc/decode_absorb.hip", "latent_kv_cache_amd/csrc/common.h"],
-    "gqa_sparse": ["latent_kv_cache_amd/csrc/decode_sparse.hip", "latent_kv_cache_amd/csrc/common.h"],
-}
-
-
-def sources_digest(paths):
-    h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def load_traffic(kernel_key, digest, workload):
-    """Counter-derived HBM bytes per launch from profiles/traffic.json, if taken on this
-    source and this workload (the records are of the flagship workload unless they name
-    another)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    try:
-        rec = json.load(open(path)).get(kernel_key)
-    except (OSError, ValueError):
-        return None
-    if not rec or rec.get("source_digest") != digest or rec.get("workload", "flagship") != workload:
-        return None
-    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(cfg, budget_s, gpu_out):
@@ -236,6 +205,7 @@ def main(argv=None):
     import synth
     from latent_kv_cache_amd import gqla
     from latent_kv_cache_amd import roofline as rf
+    from latent_kv_cache_amd.traffic import load_traffic
     from synth.device import make_workload
 
     dev = torch.device("cuda:0")
@@ -354,22 +324,20 @@ def main(argv=None):
              "gqa": path_rec(work_g, call_g, kern_g, split_g, gqa_name)}
 
     # dominant kernel: the longer of the two main attention kernels
-    digest_g = sources_digest(KERNEL_SOURCES["gqa_decode"])
-    digest_a = sources_digest(KERNEL_SOURCES["absorb_decode"])
     if kern_g >= kern_a:
         # bytes per launch: expanded rows of every cached token, queries in, outputs out
         alg = (rf.gqa_bytes_per_token(cfg.g, cfg.d_h, cfg.d_r) * total_ctx
                + q_tokens * cfg.h_q * (cfg.d_h + cfg.d_r + cfg.d_h) * 2)
         achieved = alg / (kern_g * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("gqa_decode", digest_g, args.workload),
+                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("gqa_decode", workload_desc),
                 "kernel": gqa_name, "alg_bytes_per_launch": alg, "avg_ms": round(kern_g, 4)}
     else:
         alg = (rf.absorb_bytes_per_token(cfg.r_kv, cfg.d_r) * total_ctx
                + q_tokens * cfg.h_q * (cfg.r_kv + cfg.d_r + cfg.d_h) * 2 + cfg.g * cfg.d_h * cfg.r_kv * 2)
         achieved = alg / (kern_a * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("absorb_decode", digest_a, args.workload),
+                "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": load_traffic("absorb_decode", workload_desc),
                 "kernel": absorb_name, "alg_bytes_per_launch": alg, "avg_ms": round(kern_a, 4)}
 
     note("CPU oracle baseline" if not args.no_cpu_baseline else "done timing")
