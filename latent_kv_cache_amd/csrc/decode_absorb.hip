@@ -469,7 +469,7 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     if constexpr (CS == 1) {
         if (!active) return;
 
-    #pragma unroll
+#pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
             const int rho = rho0 + 16 * rg + r16;
             const int s = row_ok[rg] ? rho / h_q : 0;
@@ -479,10 +479,10 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
             // U^T as the B operand of o^T = W_UV[j] U^T: k-step ks covers latent columns
             // 32ks + (token slot order of P), which are uacc[2ks + e/4][e%4] of this lane
             bf16x8 ub[RK / 32], ul[RK / 32];
-    #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < RK / 32; ++ks) {
                 u32x4 vh, vl;
-    #pragma unroll
+#pragma unroll
                 for (int hh = 0; hh < 4; ++hh) {
                     const floatx4& src = uacc[rg][2 * ks + (hh >> 1)];
                     const float a = src[2 * (hh & 1)] * inv, c = src[2 * (hh & 1) + 1] * inv;
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
                 for (int mt = 0; mt < DH / 16; ++mt) {
                     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
                     const u16* wrow = wj + (size_t)(mt * 16 + r16) * RK + q4 * 4;
-    #pragma unroll
+#pragma unroll
                     for (int ks = 0; ks < RK / 32; ++ks) {
                         const u32x2 lo = *reinterpret_cast<const u32x2*>(wrow + ks * 32);
                         const u32x2 hi = *reinterpret_cast<const u32x2*>(wrow + ks * 32 + 16);
