@@ -286,3 +286,14 @@ def test_full_size_long_context_sampled(gqla):
 
 if __name__ == "__main__":  # pragma: no cover
     sys.exit(pytest.main([__file__, "-v"]))
+
+
+@pytest.mark.parametrize("h_q,g,s_q", [(16, 8, 2), (64, 8, 1), (32, 4, 2), (32, 1, 1)])
+def test_absorb_column_split_rows(gqla, h_q, g, s_q):
+    """32 and 64 query rows per sequence (s_q * h_q), the workgroups whose eight waves
+    split u's latent columns in two or four parts and reduce the W_UV epilogue in LDS:
+    groups narrower than a 16-row block (h_q / g = 2 or 8: several W_UV groups per
+    block), one group wider than a block (g = 1), two query tokens per step, ragged
+    lengths across tiles and chunks."""
+    cfg = synth.config(2, g=g, s_q=s_q).with_(batch=3, h_q=h_q)
+    both_paths(cfg, [1500, 70, s_q], gqla, 3, max_ctx=1500, what=f"colsplit h_q={h_q} g={g} s_q={s_q}")
