@@ -54,18 +54,39 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int d0 = mine ? E * lane : 0;
 
     float m = kNegInf;
-    for (int p0 = 0; p0 < nvalid; p0 += NB) {
-        float lp[NB];
-#pragma unroll
-        for (int k = 0; k < NB; ++k) lp[k] = part_lse[(size_t)min(p0 + k, nvalid - 1) * plane + row];
-#pragma unroll
-        for (int k = 0; k < NB; ++k) m = fmaxf(m, lp[k]);
-    }
     float z = 0.f;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    if (m != kNegInf) {
+    // A partial with lse_p = -inf gets weight 0, so m = -inf (no chunk saw a token)
+    // leaves z = 0 and o = 0 without a separate test.
+    if (nvalid >= 1 && nvalid <= NB) {
+        // every load of the row at once: one round trip to memory (nvalid = 0, an empty
+        // sequence, takes the loop below, which loads nothing)
+        float lp[NB], po[NB][E];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const size_t pr = (size_t)min(k, nvalid - 1) * plane + row;
+            lp[k] = part_lse[pr];
+            load_e<E>(part_o + pr * d_h + d0, po[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < NB; ++k) m = fmaxf(m, lp[k]);   // clamped entries repeat the last
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const float w = (k < nvalid && lp[k] != kNegInf) ? __expf(lp[k] - m) : 0.f;
+            z += w;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += w * po[k][e];
+        }
+    } else {
+        for (int p0 = 0; p0 < nvalid; p0 += NB) {
+            float lp[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) lp[k] = part_lse[(size_t)min(p0 + k, nvalid - 1) * plane + row];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) m = fmaxf(m, lp[k]);
+        }
         for (int p0 = 0; p0 < nvalid; p0 += NB) {
             float lp[NB], po[NB][E];
 #pragma unroll
