@@ -135,15 +135,15 @@ Plan plan(const gqla_shape& s, int path, int batch, int max_ctx, int num_splits)
 // overhead (query staging, the W_UV epilogue or output write, the partial it adds to
 // the combine) in tokens: about 1000, fitted on MI355X to the absorb kernel on the
 // ragged 64K-128K workload and kept for the GQA kernel, whose time there also falls
-// with fewer, longer chunks (16 chunks 1082 us, 64 chunks 1166 us).  A plan with more chunks
-// replaces the current choice only when it is estimated 10 % faster: the estimate
-// leaves out costs that grow with the chunk count (dispatch imbalance inside a round,
-// the combine's reads), and a smaller grid also needs less workspace.  Partly filled rounds are
-// estimated as full because the dispatcher places workgroups statically (workgroup i
-// runs on XCD i mod 8, and within an XCD by a fixed rotation), so one crowded group of
-// CUs sets the time: measured at 16 sequences of 64K-128K tokens, 18-22 chunks per
-// sequence (288-352 workgroups for 256 CUs, a quarter of them empty) ran 30-60 %
-// slower than 16 chunks (256 workgroups).
+// with fewer, longer chunks (16 chunks 1082 us, 64 chunks 1166 us).  A plan with more
+// chunks replaces the current choice only when it is estimated 10 % faster: the
+// estimate leaves out costs that grow with the chunk count (dispatch imbalance inside
+// a round, the combine's reads), and a smaller grid also needs less workspace.  Partly
+// filled rounds are estimated as full because the dispatcher places workgroups
+// statically (workgroup i runs on XCD i mod 8, and within an XCD by a fixed rotation),
+// so one crowded group of CUs sets the time: measured at 16 sequences of 64K-128K
+// tokens, 18-22 chunks per sequence (288-352 workgroups for 256 CUs, a quarter of them
+// empty) ran 30-60 % slower than 16 chunks (256 workgroups).
 double split_estimate(const int32_t* lens, int batch, int max_ctx, int chunk, int mult, int slots, double ovh) {
     long long units = 0;
     int longest = 0;
@@ -320,17 +320,20 @@ gqla_status gqla_plan_splits_lens(const gqla_shape* shape, int32_t path, int32_t
         const int auto_chunk = plan(s, path, batch, max_ctx, 0).chunk;
         long long auto_units = 0;
         for (int b = 0; b < batch; ++b)
-            auto_units += (long long)mult * ((std::min(std::max(host_ctx_lens[b], 0), max_ctx) + auto_chunk - 1) / auto_chunk);
+            auto_units +=
+                (long long)mult * ((std::min(std::max(host_ctx_lens[b], 0), max_ctx) + auto_chunk - 1) / auto_chunk);
         // with four or more rounds of workgroups, partial rounds and short last chunks are
         // a small share of the time and the automatic plan stands
         if (auto_units < 4LL * slots) {
             // candidates (num_splits argument, chunks per sequence), fewest chunks first
             int cand_w[5], cand_n[5], nc = 0;
-            const int fill = slots / (batch * mult);   // chunks per sequence, one round
+            const long long fill = slots / ((long long)batch * mult);   // chunks per sequence, one round
             for (int k = 1; fill > 0 && k <= 4; ++k) {
-                const Plan pl = plan(s, path, batch, max_ctx, k * fill);
-                if (pl.n_split * batch * mult > k * slots) continue;   // chunk alignment overflowed the grid
-                cand_w[nc] = k * fill;
+                const int w = (int)(k * fill);
+                const Plan pl = plan(s, path, batch, max_ctx, w);
+                // chunk alignment can round the count up past the grid of k rounds
+                if ((long long)pl.n_split * batch * mult > (long long)k * slots) continue;
+                cand_w[nc] = w;
                 cand_n[nc++] = pl.n_split;
             }
             cand_w[nc] = 0;
