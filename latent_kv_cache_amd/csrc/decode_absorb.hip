@@ -502,7 +502,7 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
             const int jlo = (first % h_q) / hpg, jhi = (last % h_q) / hpg;
             for (int jj = jlo; jj <= jhi; ++jj) {
                 const u16* wj = w_uv + (size_t)jj * DH * RK;
-    #pragma unroll 2
+#pragma unroll 2
                 for (int mt = 0; mt < DH / 16; ++mt) {
                     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
                     const u16* wrow = wj + (size_t)(mt * 16 + r16) * RK + q4 * 4;
