@@ -24,8 +24,11 @@
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers, owned by the caller, in the
  *     dtype of shape->dtype (bf16 or fp32; one dtype per call), row-major.
- *     ctx_lens is a device int32[batch].  The library allocates nothing and
- *     keeps no state besides a per-device cache of the compute-unit count.
+ *     ctx_lens is a device int32[batch].  The library allocates nothing.  Its
+ *     state: a per-device cache of the compute-unit count; per thread, the last
+ *     error message and the optional timing events of gqla_set_kernel_events;
+ *     and the static device scratch of gqla_decode_gqa_noalloc (one copy per
+ *     device, with its address looked up once per device).
  *   - q_rope and the k_R columns of the cache hold keys/queries with the
  *     rotary embedding already applied.
  *   - stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
@@ -36,7 +39,7 @@
  *   - ctx_lens contents are not read on the host.  Kernels clamp L_b to
  *     [0, max_ctx]; a query that sees no row returns o = 0, lse = -inf.
  *   - Thread safety: calls are reentrant; concurrent calls must use distinct
- *     workspaces.
+ *     workspaces (gqla_decode_gqa_noalloc: see its note on overlapping calls).
  */
 #ifndef GQLA_H
 #define GQLA_H
@@ -147,6 +150,33 @@ gqla_status gqla_decode_gqa(const gqla_shape* shape, int32_t batch, int32_t max_
                             const int32_t* ctx_lens, void* out, float* lse,
                             void* workspace, size_t workspace_bytes,
                             int32_t num_splits, void* stream);
+
+/* Largest scratch, in bytes, that gqla_decode_gqa_noalloc may use (64 MiB). */
+#define GQLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* gqla_decode_gqa for callers that cannot allocate device memory or pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same kernels, same split plan and bit-identical results as gqla_decode_gqa with the
+ * same arguments, but the split-K partials live in a static device array of
+ * GQLA_NOALLOC_SCRATCH_BYTES compiled into the library instead of a caller workspace.
+ *   - The call allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   - It runs on the current device.  Each device the library runs on holds its own
+ *     copy of the array until the process ends; the first call on a device looks up
+ *     that copy's address (hipGetSymbolAddress) with the device current.
+ *   - All calls on one device share its array, which keeps the last call's contents.
+ *     Calls ordered on one stream are safe; calls that overlap on one device (two
+ *     streams, or two threads without ordering between them) race, and their results
+ *     are undefined.  Nothing in the array needs clearing: every partial the split-K
+ *     merge reads is written earlier by the same call.
+ *   - Errors: those of gqla_decode_gqa, and GQLA_ERR_WORKSPACE when the call needs more
+ *     than GQLA_NOALLOC_SCRATCH_BYTES (gqla_workspace_size with GQLA_PATH_GQA and the
+ *     same arguments gives the need); such a call enqueues nothing.  Fewer sequences
+ *     per call or a smaller num_splits lower the need. */
+gqla_status gqla_decode_gqa_noalloc(const gqla_shape* shape, int32_t batch, int32_t max_ctx,
+                                    const void* q_nope, const void* q_rope,
+                                    const void* group_cache, int64_t group_bstride,
+                                    const int32_t* ctx_lens, void* out, float* lse,
+                                    int32_t num_splits, void* stream);
 
 /* Sparse GQLA decode (section 2, Sparse GQLA: fine-grained sparse attention keeps the
  * GQA path, since a group's h_q/g = 16 heads fill one 16-row matrix tile).  Query

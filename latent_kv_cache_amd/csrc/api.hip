@@ -4,10 +4,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gqla.h"
 #include "launch.h"
@@ -30,18 +32,36 @@ gqla_status ok() {
     return GQLA_OK;
 }
 
-// Compute units of the current device, cached per device id.
+// Compute units of the current device, cached per device id.  Concurrent first calls
+// may both query the attribute; they store the same value, and the atomics make the
+// cache safe to read and write from several threads.
 int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int cus = 0;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        cached[dev] = cus;
+        cached[dev].store(cus, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return cus;
 }
+
+// Device-resident scratch of gqla_decode_gqa_noalloc: the split-K partials of a call
+// live here instead of in a caller workspace.  Every device the library runs on holds
+// its own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is taken once per device with
+// hipGetSymbolAddress (on that device's first no-allocation call, with the device
+// current) and only that address is ever handed to kernels.
+constexpr size_t kNoAllocScratchBytes = GQLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[64];
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -203,10 +223,30 @@ gqla_status hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
+// Device address of the current device's copy of `scratch` (looked up once per device).
+gqla_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(GQLA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..63", dev);
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] {
+        void* p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        slot.ptr = slot.err == hipSuccess ? p : nullptr;
+    });
+    if (slot.err != hipSuccess) return hip_status(slot.err, "hipGetSymbolAddress(scratch)");
+    if (!slot.ptr) return fail(GQLA_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    *out = slot.ptr;
+    return GQLA_OK;
+}
+
+// use_scratch: the partials go to the static device scratch instead of `workspace`
+// (which is then ignored); a call needing more than its size fails before any launch.
 gqla_status decode_common(int path, const gqla_shape* sp, int32_t batch, int32_t max_ctx, const void* q_nope,
                           const void* q_rope, const void* w_uk, const void* w_uv, const void* cache,
                           int64_t bstride, const int32_t* ctx_lens, void* out, float* lse, void* workspace,
-                          size_t workspace_bytes, int32_t num_splits, void* stream) {
+                          size_t workspace_bytes, int32_t num_splits, void* stream, bool use_scratch = false) {
     TRY(check_shape(sp, path));
     TRY(check_sizes(batch, max_ctx));
     if (num_splits < 0) return fail(GQLA_ERR_INVALID_ARG, "num_splits=%d < 0", num_splits);
@@ -226,10 +266,19 @@ gqla_status decode_common(int path, const gqla_shape* sp, int32_t batch, int32_t
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(GQLA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
     const Plan p = plan(s, path, batch, max_ctx, num_splits);
     const Layout lay = layout(s, path, batch, p);
-    if (!workspace) return fail(GQLA_ERR_WORKSPACE, "workspace is null (%zu bytes needed)", lay.total);
-    if (!aligned16(workspace)) return fail(GQLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    if (workspace_bytes < lay.total)
-        return fail(GQLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, lay.total);
+    if (use_scratch) {
+        if (lay.total > kNoAllocScratchBytes)
+            return fail(GQLA_ERR_WORKSPACE,
+                        "the call needs %zu bytes of scratch, above the static maximum of %zu "
+                        "(use fewer sequences per call or a smaller num_splits)",
+                        lay.total, kNoAllocScratchBytes);
+        TRY(scratch_address(&workspace));
+    } else {
+        if (!workspace) return fail(GQLA_ERR_WORKSPACE, "workspace is null (%zu bytes needed)", lay.total);
+        if (!aligned16(workspace)) return fail(GQLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+        if (workspace_bytes < lay.total)
+            return fail(GQLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, lay.total);
+    }
 
     gqla::DecodeArgs a;
     a.h_q = s.h_q;
@@ -412,6 +461,14 @@ gqla_status gqla_decode_gqa(const gqla_shape* shape, int32_t batch, int32_t max_
                             int32_t num_splits, void* stream) {
     return decode_common(GQLA_PATH_GQA, shape, batch, max_ctx, q_nope, q_rope, nullptr, nullptr, group_cache,
                          group_bstride, ctx_lens, out, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+gqla_status gqla_decode_gqa_noalloc(const gqla_shape* shape, int32_t batch, int32_t max_ctx, const void* q_nope,
+                                    const void* q_rope, const void* group_cache, int64_t group_bstride,
+                                    const int32_t* ctx_lens, void* out, float* lse, int32_t num_splits,
+                                    void* stream) {
+    return decode_common(GQLA_PATH_GQA, shape, batch, max_ctx, q_nope, q_rope, nullptr, nullptr, group_cache,
+                         group_bstride, ctx_lens, out, lse, nullptr, 0, num_splits, stream, true);
 }
 
 gqla_status gqla_decode_gqa_sparse(const gqla_shape* shape, int32_t batch, int32_t max_ctx, const void* q_nope,

@@ -21,10 +21,11 @@ LIB_PATH = os.path.join(PKG, "libgqla.so")
 
 BF16, F32 = 0, 1
 ABSORB, GQA, SPARSE = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GQLA_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "GQLA_OK", 1: "GQLA_ERR_INVALID_ARG", 2: "GQLA_ERR_UNSUPPORTED", 3: "GQLA_ERR_WORKSPACE", 4: "GQLA_ERR_HIP"}
 
 EXPORTS = ("gqla_workspace_size", "gqla_plan_splits", "gqla_plan_splits_lens", "gqla_expand_groups", "gqla_decode_absorb",
-           "gqla_decode_gqa", "gqla_decode_gqa_sparse", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
+           "gqla_decode_gqa", "gqla_decode_gqa_noalloc", "gqla_decode_gqa_sparse", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
            "gqla_set_kernel_events", "gqla_status_string", "gqla_last_error")
 
 
@@ -75,6 +76,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        c_vp, c_sz, c_i32, c_vp]
     lib.gqla_decode_gqa.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_sz,
                                     c_i32, c_vp]
+    lib.gqla_decode_gqa_noalloc.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_i32, c_vp]
     lib.gqla_decode_gqa_sparse.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_vp,
                                            c_vp, c_sz, c_i32, c_vp]
     lib.gqla_append_rows.argtypes = [sp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_i64,
@@ -84,7 +86,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        c_vp]
     lib.gqla_set_kernel_events.argtypes = [c_vp, c_vp]
     for name in ("gqla_workspace_size", "gqla_plan_splits", "gqla_plan_splits_lens", "gqla_expand_groups", "gqla_decode_absorb",
-                 "gqla_decode_gqa", "gqla_decode_gqa_sparse", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
+                 "gqla_decode_gqa", "gqla_decode_gqa_noalloc", "gqla_decode_gqa_sparse", "gqla_append_rows", "gqla_select_path", "gqla_measure_peaks",
                  "gqla_set_kernel_events"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gqla_status_string.argtypes = [ctypes.c_int]
@@ -210,6 +212,18 @@ def decode_gqa(shape: Shape, q_nope, q_rope, group_cache, ctx_lens, out, lse=Non
     _check(load().gqla_decode_gqa(ctypes.byref(shape), batch, max_ctx, _ptr(q_nope), _ptr(q_rope),
                                   _ptr(group_cache), gbs, _ptr(ctx_lens), _ptr(out), _ptr(lse), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), num_splits, _stream(stream)))
+    return out
+
+
+def decode_gqa_noalloc(shape: Shape, q_nope, q_rope, group_cache, ctx_lens, out, lse=None, num_splits: int = 0,
+                       stream=None):
+    """decode_gqa with the split-K partials in the library's static device scratch (no
+    workspace, no allocation by the library; overlapping calls on one device race)."""
+    gbs, max_ctx = _rows(group_cache, 2 * shape.g * shape.d_h + shape.d_r)
+    batch = group_cache.shape[0]
+    _check(load().gqla_decode_gqa_noalloc(ctypes.byref(shape), batch, max_ctx, _ptr(q_nope), _ptr(q_rope),
+                                          _ptr(group_cache), gbs, _ptr(ctx_lens), _ptr(out), _ptr(lse), num_splits,
+                                          _stream(stream)))
     return out
 
 

@@ -142,6 +142,30 @@ def test_decode_argument_validation(lib):
                                 0, 0, None) == 0
 
 
+def test_noalloc_validation_and_limit(lib):
+    """The no-allocation GQA decode validates like the workspace call and rejects a call
+    whose partials exceed the static scratch (GQLA_ERR_WORKSPACE) before any launch."""
+    L = gqla.load()
+    sh = FLAG
+    width = 2 * 8 * 128 + 64
+
+    def call(B, S, splits, **over):
+        a = dict(q_nope=FAKE, q_rope=FAKE, gc=FAKE, gbs=S * width, lens=FAKE, out=FAKE, lse=None)
+        a.update(over)
+        return L.gqla_decode_gqa_noalloc(ctypes.byref(sh), B, S, a["q_nope"], a["q_rope"], a["gc"], a["gbs"],
+                                         a["lens"], a["out"], a["lse"], splits, None)
+
+    assert call(2, 64, 0, q_nope=None) == 1
+    assert call(2, 64, 0, gbs=64 * width - 8) == 1
+    assert call(2, 64, 0, lens=None) == 1
+    assert call(2, 64, -1) == 1
+    B, S, splits = 64, 32768, 64
+    assert ws_size(sh, gqla.GQA, B, S, splits)[1] > gqla.NOALLOC_SCRATCH_BYTES
+    assert call(B, S, splits) == 3
+    assert b"static maximum" in L.gqla_last_error()
+    assert L.gqla_decode_gqa_noalloc(ctypes.byref(sh), 0, S, None, None, None, 0, None, None, None, 0, None) == 0
+
+
 def test_expand_argument_validation(lib):
     L = gqla.load()
     sh = FLAG
