@@ -172,6 +172,58 @@ def _rows(t, width: int) -> Tuple[int, int]:
     return int(t.stride(0)), int(t.shape[1])
 
 
+def _torch_dtype(shape: Shape):
+    import torch
+    if shape.dtype == BF16:
+        return torch.bfloat16
+    if shape.dtype == F32:
+        return torch.float32
+    raise ValueError(f"shape.dtype {shape.dtype} is neither BF16 ({BF16}) nor F32 ({F32})")
+
+
+def _validate(device, **specs) -> None:
+    """Check tensors before any library call: each spec is (tensor, expected shape, dtype);
+    a tensor must have exactly that shape and dtype, be contiguous, and live on `device`
+    (a CUDA device).  A None tensor is skipped.  Raises ValueError naming the argument."""
+    for name, (t, want_shape, want_dtype) in specs.items():
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(want_shape):
+            raise ValueError(f"{name} must have shape {tuple(want_shape)}, got {tuple(t.shape)}")
+        if t.dtype != want_dtype:
+            raise ValueError(f"{name} must be {want_dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, (t, _, _) in specs.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} is on {t.device}; every tensor of the call must be on the cache's "
+                             f"CUDA device ({device})")
+
+
+def _cache(name: str, t, shape: Shape, width: int) -> Tuple[int, int, int]:
+    """(batch, batch stride, max_ctx) of a cache tensor, checked for dtype and CUDA placement."""
+    if t.dtype != _torch_dtype(shape):
+        raise ValueError(f"{name} must be {_torch_dtype(shape)} (shape.dtype), got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor, got {t.device}")
+    bs, max_ctx = _rows(t, width)
+    return int(t.shape[0]), bs, max_ctx
+
+
+def _decode_specs(shape: Shape, batch: int, q_nope, q_rope, ctx_lens, out, lse, workspace=None):
+    import torch
+    dt = _torch_dtype(shape)
+    q = (batch, shape.s_q, shape.h_q)
+    specs = dict(q_nope=(q_nope, q + (shape.d_h,), dt), q_rope=(q_rope, q + (shape.d_r,), dt),
+                 ctx_lens=(ctx_lens, (batch,), torch.int32), out=(out, q + (shape.d_h,), dt),
+                 lse=(lse, q, torch.float32))
+    if workspace is not None:
+        specs["workspace"] = (workspace, (workspace.numel(),), workspace.dtype)
+    return specs
+
+
 def alloc_workspace(shape: Shape, path: int, batch: int, max_ctx: int, num_splits: int = 0, device=None):
     import torch
     n = workspace_size(shape, path, batch, max_ctx, num_splits)
@@ -180,10 +232,14 @@ def alloc_workspace(shape: Shape, path: int, batch: int, max_ctx: int, num_split
 
 def expand_groups(shape: Shape, latent, w_uk, w_uv, ctx_lens, group_cache, row_begin: int = 0, stream=None):
     """Write group rows [row_begin, L_b) of group_cache [B][S][2 g d_h + d_r] from latent [B][S][r_kv + d_r]."""
-    lbs, max_ctx = _rows(latent, shape.r_kv + shape.d_r)
-    gbs, gctx = _rows(group_cache, 2 * shape.g * shape.d_h + shape.d_r)
-    if gctx < max_ctx:
-        raise ValueError("group_cache holds fewer rows per sequence than latent")
+    import torch
+    batch, lbs, max_ctx = _cache("latent", latent, shape, shape.r_kv + shape.d_r)
+    gb, gbs, gctx = _cache("group_cache", group_cache, shape, 2 * shape.g * shape.d_h + shape.d_r)
+    if gb != batch or gctx < max_ctx:
+        raise ValueError("group_cache must hold as many sequences and at least as many rows as latent")
+    w = (shape.g, shape.d_h, shape.r_kv)
+    _validate(latent.device, w_uk=(w_uk, w, latent.dtype), w_uv=(w_uv, w, latent.dtype),
+              ctx_lens=(ctx_lens, (batch,), torch.int32), group_cache=(group_cache, group_cache.shape, latent.dtype))
     _check(load().gqla_expand_groups(ctypes.byref(shape), latent.shape[0], max_ctx, _ptr(latent), lbs, _ptr(w_uk),
                                      _ptr(w_uv), _ptr(ctx_lens), row_begin, _ptr(group_cache), gbs, _stream(stream)))
 
@@ -191,8 +247,10 @@ def expand_groups(shape: Shape, latent, w_uk, w_uv, ctx_lens, group_cache, row_b
 def decode_absorb(shape: Shape, q_nope, q_rope, w_uk, w_uv, latent, ctx_lens, out, lse=None, workspace=None,
                   num_splits: int = 0, stream=None):
     """MQA-absorb decode into out [B][s_q][h_q][d_h] (and lse [B][s_q][h_q] if given)."""
-    lbs, max_ctx = _rows(latent, shape.r_kv + shape.d_r)
-    batch = latent.shape[0]
+    batch, lbs, max_ctx = _cache("latent", latent, shape, shape.r_kv + shape.d_r)
+    w = (shape.g, shape.d_h, shape.r_kv)
+    _validate(latent.device, w_uk=(w_uk, w, latent.dtype), w_uv=(w_uv, w, latent.dtype),
+              **_decode_specs(shape, batch, q_nope, q_rope, ctx_lens, out, lse, workspace))
     if workspace is None:
         workspace = alloc_workspace(shape, ABSORB, batch, max_ctx, num_splits, latent.device)
     _check(load().gqla_decode_absorb(ctypes.byref(shape), batch, max_ctx, _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
@@ -205,8 +263,8 @@ def decode_absorb(shape: Shape, q_nope, q_rope, w_uk, w_uv, latent, ctx_lens, ou
 def decode_gqa(shape: Shape, q_nope, q_rope, group_cache, ctx_lens, out, lse=None, workspace=None,
                num_splits: int = 0, stream=None):
     """GQA decode over expanded rows into out [B][s_q][h_q][d_h] (and lse if given)."""
-    gbs, max_ctx = _rows(group_cache, 2 * shape.g * shape.d_h + shape.d_r)
-    batch = group_cache.shape[0]
+    batch, gbs, max_ctx = _cache("group_cache", group_cache, shape, 2 * shape.g * shape.d_h + shape.d_r)
+    _validate(group_cache.device, **_decode_specs(shape, batch, q_nope, q_rope, ctx_lens, out, lse, workspace))
     if workspace is None:
         workspace = alloc_workspace(shape, GQA, batch, max_ctx, num_splits, group_cache.device)
     _check(load().gqla_decode_gqa(ctypes.byref(shape), batch, max_ctx, _ptr(q_nope), _ptr(q_rope),
@@ -219,8 +277,8 @@ def decode_gqa_noalloc(shape: Shape, q_nope, q_rope, group_cache, ctx_lens, out,
                        stream=None):
     """decode_gqa with the split-K partials in the library's static device scratch (no
     workspace, no allocation by the library; overlapping calls on one device race)."""
-    gbs, max_ctx = _rows(group_cache, 2 * shape.g * shape.d_h + shape.d_r)
-    batch = group_cache.shape[0]
+    batch, gbs, max_ctx = _cache("group_cache", group_cache, shape, 2 * shape.g * shape.d_h + shape.d_r)
+    _validate(group_cache.device, **_decode_specs(shape, batch, q_nope, q_rope, ctx_lens, out, lse))
     _check(load().gqla_decode_gqa_noalloc(ctypes.byref(shape), batch, max_ctx, _ptr(q_nope), _ptr(q_rope),
                                           _ptr(group_cache), gbs, _ptr(ctx_lens), _ptr(out), _ptr(lse), num_splits,
                                           _stream(stream)))
@@ -231,11 +289,13 @@ def decode_gqa_sparse(shape: Shape, q_nope, q_rope, group_cache, ctx_lens, indic
                       num_splits: int = 0, stream=None):
     """Sparse GQLA decode: query token s of group j attends to the rows listed in
     indices [B][s_q][g][topk] (int32; -1 pads) of group_cache [B][S][2 g d_h + d_r]."""
-    gbs, max_ctx = _rows(group_cache, 2 * shape.g * shape.d_h + shape.d_r)
-    batch = group_cache.shape[0]
+    import torch
+    batch, gbs, max_ctx = _cache("group_cache", group_cache, shape, 2 * shape.g * shape.d_h + shape.d_r)
     if indices.dim() != 4 or tuple(indices.shape[:3]) != (batch, shape.s_q, shape.g) or not indices.is_contiguous():
         raise ValueError(f"indices must be a contiguous [B][s_q][g][topk] tensor, got {tuple(indices.shape)}")
     topk = int(indices.shape[3])
+    _validate(group_cache.device, indices=(indices, indices.shape, torch.int32),
+              **_decode_specs(shape, batch, q_nope, q_rope, ctx_lens, out, lse, workspace))
     if workspace is None:
         workspace = alloc_workspace(shape, SPARSE, batch, topk, num_splits, group_cache.device)
     _check(load().gqla_decode_gqa_sparse(ctypes.byref(shape), batch, max_ctx, _ptr(q_nope), _ptr(q_rope),
@@ -250,12 +310,21 @@ def append_rows(shape: Shape, c_new, kr_new, ctx_lens, latent, q_rope_raw=None, 
     """Decode-step append: write the s_q new rows of every sequence into latent [B][S][r_kv + d_r]
     (c_new [B][s_q][r_kv], kr_new [B][s_q][d_r] rotated at t = L_b - s_q + s), rotate q_rope_raw
     into q_rope_out, and expand the new rows into group_cache [B][S][2 g d_h + d_r] if given."""
-    lbs, max_ctx = _rows(latent, shape.r_kv + shape.d_r)
+    import torch
+    batch, lbs, max_ctx = _cache("latent", latent, shape, shape.r_kv + shape.d_r)
     gbs = 0
     if group_cache is not None:
-        gbs, gctx = _rows(group_cache, 2 * shape.g * shape.d_h + shape.d_r)
-        if gctx < max_ctx:
-            raise ValueError("group_cache holds fewer rows per sequence than latent")
+        gb, gbs, gctx = _cache("group_cache", group_cache, shape, 2 * shape.g * shape.d_h + shape.d_r)
+        if gb != batch or gctx < max_ctx:
+            raise ValueError("group_cache must hold as many sequences and at least as many rows as latent")
+    dt = latent.dtype
+    qr = (batch, shape.s_q, shape.h_q, shape.d_r)
+    w = (shape.g, shape.d_h, shape.r_kv)
+    _validate(latent.device, c_new=(c_new, (batch, shape.s_q, shape.r_kv), dt),
+              kr_new=(kr_new, (batch, shape.s_q, shape.d_r), dt), ctx_lens=(ctx_lens, (batch,), torch.int32),
+              q_rope_raw=(q_rope_raw, qr, dt), q_rope_out=(q_rope_out, qr, dt),
+              w_uk=(w_uk, w, dt), w_uv=(w_uv, w, dt),
+              group_cache=(group_cache, None if group_cache is None else group_cache.shape, dt))
     _check(load().gqla_append_rows(ctypes.byref(shape), latent.shape[0], max_ctx, _ptr(c_new), _ptr(kr_new),
                                    _ptr(q_rope_raw), _ptr(q_rope_out), float(rope_theta), _ptr(ctx_lens),
                                    _ptr(latent), lbs, _ptr(w_uk), _ptr(w_uv), _ptr(group_cache), gbs,

@@ -297,3 +297,22 @@ def test_absorb_column_split_rows(gqla, h_q, g, s_q):
     lengths across tiles and chunks."""
     cfg = synth.config(2, g=g, s_q=s_q).with_(batch=3, h_q=h_q)
     both_paths(cfg, [1500, 70, s_q], gqla, 3, max_ctx=1500, what=f"colsplit h_q={h_q} g={g} s_q={s_q}")
+
+
+def test_binding_rejects_mismatched_tensors(gqla):
+    """A host ctx_lens, int64 lengths, an output of the wrong dtype or size, or weights of
+    the wrong shape raise ValueError in the binding; nothing is launched."""
+    torch = gu.torch_mod()
+    cfg = synth.config(3).with_(batch=2)
+    w = gu.workload(cfg, lens=[40, 3], max_ctx=64)
+    sh = gu.shape_of(cfg, gqla)
+    out = torch.zeros((2, 1, cfg.h_q, cfg.d_h), dtype=torch.bfloat16, device="cuda")
+    args = (sh, w.q_nope, w.q_rope, w.w_uk, w.w_uv, w.latent)
+    for lens, o, msg in ((w.ctx_lens.cpu(), out, "ctx_lens"), (w.ctx_lens.long(), out, "ctx_lens must be"),
+                         (w.ctx_lens, out.float(), "out must be"), (w.ctx_lens, out[:1], "out must have shape")):
+        with pytest.raises(ValueError, match=msg):
+            gqla.decode_absorb(*args, lens, o)
+    with pytest.raises(ValueError, match="w_uk must have shape"):
+        gqla.decode_absorb(sh, w.q_nope, w.q_rope, w.w_uk[:4], w.w_uv, w.latent, w.ctx_lens, out)
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 0))
