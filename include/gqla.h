@@ -31,6 +31,12 @@
  *     device, with its address looked up once per device).
  *   - q_rope and the k_R columns of the cache hold keys/queries with the
  *     rotary embedding already applied.
+ *   - Operand range (bf16 storage): the kernels multiply fp16 copies of the bf16
+ *     inputs on the MFMA units.  Values whose magnitude lies in fp16's normal range
+ *     [2^-14, 65504] are converted exactly; smaller magnitudes keep fp16's subnormal
+ *     spacing 2^-24 (an absolute error of at most 2^-24 per element); magnitudes above
+ *     65504 are outside the supported range (they saturate).  This applies to the
+ *     latent rows, k_R, the queries, the expanded rows of the GQA path and W_UK / W_UV.
  *   - stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *     work on it and never synchronise; results are ready when the stream is.
  *   - Arguments are validated on the host before any launch; a failed check
@@ -74,7 +80,7 @@ typedef struct gqla_shape {
 } gqla_shape;
 
 /* Bytes of device workspace a decode call needs (split-K partials, and for the
- * absorb path the absorbed queries).  num_splits: 0 = automatic, else an upper
+ * absorb path one absorbed-query record per query row).  num_splits: 0 = automatic, else an upper
  * bound on context chunks per sequence.  For GQLA_PATH_SPARSE the max_ctx argument
  * is the index-list length topk (the chunks split the list).  Returns GQLA_OK and
  * writes *bytes. */
@@ -123,9 +129,11 @@ gqla_status gqla_expand_groups(const gqla_shape* shape, int32_t batch, int32_t m
                                const int32_t* ctx_lens, int32_t row_begin,
                                void* group_cache, int64_t group_bstride, void* stream);
 
-/* MQA-absorb decode (section 2, memory-friendly path, "identical to MLA"):
- * q~ = W_UK[j]^T q_nope per head, scores s_t = scale [q~ | q_rope].[c_t | k_R,t],
- * u = softmax-weighted sum of c_t, o = W_UV[j] u.
+/* MQA-absorb decode (section 2, memory-friendly path: the MLA form with group-indexed
+ * up-projections): q~ = W_UK[j]^T q_nope per head, scores
+ * s_t = scale [q~ | q_rope].[c_t | k_R,t], u = softmax-weighted sum of c_t,
+ * o = W_UV[j] u.  The absorbed query is carried to about 22 significant bits, so the
+ * result keeps the bf16 tolerance however peaked the softmax is.
  *   q_nope [batch][s_q][h_q][d_h], q_rope [batch][s_q][h_q][d_r]
  *   w_uk, w_uv [g][d_h][r_kv]; latent as in gqla_expand_groups
  *   out [batch][s_q][h_q][d_h] (dtype); lse (nullable) fp32 [batch][s_q][h_q],

@@ -130,7 +130,11 @@ Plan plan(const gqla_shape& s, int path, int batch, int max_ctx, int num_splits)
         }
         const int cus = device_cus();
         want = (cus * per_cu + units - 1) / units;
-        const int by_len = (ctx + 4095) / 4096;
+        // chunks of at most 4096 tokens (8192 on the bf16 absorb path, whose workgroups
+        // hold 64 query rows and one of them fills a CU's LDS; one chunk per sequence
+        // also lets its kernel write the result without a combine)
+        const int max_chunk = (s.dtype == GQLA_BF16 && path == GQLA_PATH_ABSORB) ? 8192 : 4096;
+        const int by_len = (ctx + max_chunk - 1) / max_chunk;
         if (by_len > want) want = by_len;
     }
     if (want > ctx) want = ctx;
@@ -187,7 +191,7 @@ Layout layout(const gqla_shape& s, int path, int batch, const Plan& p) {
     l.part_lse = align256(l.part_o + (size_t)p.n_split * rows * s.d_h * sizeof(float));
     l.qhat = align256(l.part_lse + (size_t)p.n_split * rows * sizeof(float));
     size_t end = l.qhat;
-    if (path == GQLA_PATH_ABSORB && s.dtype == GQLA_BF16) end = align256(l.qhat + rows * (s.r_kv + s.d_r) * 2);
+    if (path == GQLA_PATH_ABSORB && s.dtype == GQLA_BF16) end = align256(l.qhat + rows * gqla::absorb_qrec_bytes());
     l.total = end;
     return l;
 }
@@ -316,6 +320,8 @@ gqla_status decode_common(int path, const gqla_shape* sp, int32_t batch, int32_t
         e = path == GQLA_PATH_ABSORB ? gqla::launch_absorb_f32(a, st) : gqla::launch_gqa_f32(a, st);
     }
     if (e != hipSuccess) return hip_status(e, "decode launch");
+    // the bf16 absorb kernel writes the result itself when each sequence is one chunk
+    if (s.dtype == GQLA_BF16 && path == GQLA_PATH_ABSORB && p.n_split == 1) return ok();
     return hip_status(gqla::launch_combine(a, s.dtype == GQLA_BF16, st), "combine launch");
 }
 
@@ -357,7 +363,9 @@ gqla_status gqla_plan_splits_lens(const gqla_shape* shape, int32_t path, int32_t
     int best = 0;
     if (s.dtype == GQLA_BF16 && (path == GQLA_PATH_ABSORB || path == GQLA_PATH_GQA) && batch > 0 && max_ctx > 0) {
         int mult = 1, per_cu = 1;
-        const double ovh = 1000.0;
+        // per-workgroup overhead in tokens: the absorb workgroup also stages its queries,
+        // fills a two-tile pipeline and runs the W_UV epilogue for 64 rows
+        const double ovh = path == GQLA_PATH_ABSORB ? 4000.0 : 1000.0;
         if (path == GQLA_PATH_ABSORB) {
             const int rows = gqla::absorb_block_rows(s.s_q * s.h_q);
             mult = (s.s_q * s.h_q + rows - 1) / rows;

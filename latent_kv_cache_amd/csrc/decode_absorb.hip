@@ -4,11 +4,12 @@
 // Method: "GQLA: Group-Query Latent Attention for Hardware-Adaptive LLM
 // Decoding", technical summary section 2 (Architecture, MQA-absorb path).  Head i
 // of group j = i / (h_q/g) attends over the shared latent rows [c_t | k_R,t]:
-//   q~ = W_UK[j]^T q^N,  score_t = scale [q~ | q^R].[c_t | k_R,t],
+//   q~ = W_UK[j]^T q^N,  score_t = scale ([q~ | q^R].[c_t | k_R,t]),
 //   u = sum_t softmax(score)_t c_t,  o = W_UV[j] u,
 // over the visible tokens t <= L_b - s_q + s of query token s, one context chunk per
-// workgroup (split-K); each workgroup writes the chunk's o and log-sum-exp and
-// launch_combine merges the chunks.
+// workgroup (split-K).  With one chunk per sequence the workgroup writes o and the
+// log-sum-exp itself; otherwise it writes the chunk's partials and launch_combine
+// merges them.
 #include "common.h"
 #include "launch.h"
 
@@ -22,50 +23,39 @@ constexpr int RK = 512;   // latent width
 constexpr int W = RK + DR;
 constexpr int TT = 32;    // tokens per tile
 
+// Absorbed-query record of one query row, written by the prologue and read once by the
+// attention kernel (QREC bytes, 16-byte aligned):
+//   [0, 1024)     hi: fp16 of x' = q~ * scale * log2(e) * 2^E, latent column order
+//   [1024, 2048)  lo: fp16 of x' - hi (the rounding residual of hi, rounded again)
+//   [2048, 2176)  q^R as fp16 (exact for bf16 inputs in fp16's range), unscaled
+//   [2176, 2180)  2^-E (fp32); 2^E is a per-row power of two that puts max |x'| in
+//                 [2^13, 2^14), so hi stays finite and lo stays in fp16's normal range
+// hi + lo carries q~ to about 22 significant bits.  A single fp16 rounding of q~
+// (11 bits) gives score errors that grow with |score|: with sharp softmaxes (peak
+// logits of 30-40 in log2 units) they alone exceed the 2e-3 + 2e-2 |o| bound
+// several-fold, which the hi + lo pair removes at one extra MFMA per latent k-step.
+constexpr int QREC = 2192;
+constexpr int QHI = 0, QLO = 1024, QROPE = 2048, QINV = 2176;
+
 // ---------------------------------------------------------------------------
-// Prologue: qhat[b][rho][0:512] = W_UK[j]^T q^N * scale * log2(e) and
-// qhat[b][rho][512:576] = q^R * scale * log2(e), rho = s*h_q + h, stored as fp16 (the
-// operand type of the attention kernel's MFMA).  With the softmax scale and the
-// change of base folded into the query, the attention kernel's scores come out as
-// log2-domain logits and need no multiply.
-// grid = (row blocks of 64, g, 4 quarters of the latent columns); block = 4 waves.
-// Rows of group j are numbered iota = (b*s_q + s)*hpg + hh.  The block's quarter of
-// W_UK[j] ([d][r], 128 x 128, 32 KB) is staged row-major in LDS, so four blocks fit on
-// a CU; the contraction runs over d, so the A operand (W_UK^T) is formed with
-// transposing LDS reads: 4 rows d x 16 columns r per 16-lane group.  The blocks of the
-// first quarter also write the scaled q^R.
+// Prologue: one block per (64 rows of group j, j); 4 waves of 16 rows.  Rows of group j
+// are numbered iota = (b*s_q + s)*hpg + hh.  The contraction runs over d, strided in the
+// [g][d_h][r_kv] layout, so each quarter of W_UK[j]'s columns (128 d x 128 r, 36 KB with
+// the pad) is staged row-major in LDS and the A operand (W_UK^T) is formed with
+// transposing LDS reads: 4 rows d x 16 columns r per 16-lane group.  A lane ends with
+// the 128 columns 16 mt + 4 q4 + i (mt = 0..31, i = 0..3) of its row r16.
 // ---------------------------------------------------------------------------
 constexpr int PRO_COLS = RK / 4;
 constexpr int PRO_STRIDE = PRO_COLS + 16;
 
 __global__ __launch_bounds__(256) void absorb_prologue_kernel(
     const u16* __restrict__ q_nope, const u16* __restrict__ q_rope, const u16* __restrict__ w_uk,
-    u16* __restrict__ qhat, int batch, int h_q, int g, int s_q, float scale_log2) {
+    unsigned char* __restrict__ qrec, int batch, int h_q, int g, int s_q, float scale_log2) {
     __shared__ __attribute__((aligned(16))) u16 wt[DH * PRO_STRIDE];
     const int j = blockIdx.y;
-    const int r0 = blockIdx.z * PRO_COLS;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int q4 = lane >> 4, r16 = lane & 15;
-
-    // stage columns r0 .. r0+127 of W_UK[j]: 2048 chunks of 16 bytes, 8 per thread, all
-    // eight loads in flight before the first store
-    const u16* wj = w_uk + (size_t)j * DH * RK + r0;
-    constexpr int CPRW = PRO_COLS / 8;   // 16-byte chunks per staged row
-    {
-        u32x4 v[DH * CPRW / 256];
-#pragma unroll
-        for (int k = 0; k < DH * CPRW / 256; ++k) {
-            const int c = k * 256 + tid;
-            v[k] = *reinterpret_cast<const u32x4*>(wj + (size_t)(c / CPRW) * RK + (c % CPRW) * 8);
-        }
-#pragma unroll
-        for (int k = 0; k < DH * CPRW / 256; ++k) {
-            const int c = k * 256 + tid;
-            *reinterpret_cast<u32x4*>(wt + (c / CPRW) * PRO_STRIDE + (c % CPRW) * 8) = v[k];
-        }
-    }
-    __syncthreads();
 
     const int hpg = h_q / g;
     const int nrows = batch * s_q * hpg;
@@ -76,8 +66,7 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
     const int b = bs / s_q, s = bs - (bs / s_q) * s_q;
     const int h = j * hpg + hh;
     const size_t qrow = ((size_t)b * s_q + s) * h_q + h;
-    const int RQ = s_q * h_q;
-    u16* dst = qhat + ((size_t)b * RQ + (size_t)s * h_q + h) * W;
+    unsigned char* dst = qrec + qrow * QREC;
 
     // k-slot e of lane group q4 in k-step kd is d = 32kd + 4q4 + e (e < 4) or
     // 32kd + 16 + 4q4 + (e - 4): the transposing reads of the four lane groups then lie
@@ -94,85 +83,158 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
         }
     }
 
-    // A operand lane (q4, r16), k-step kd: W_UK[d(kd, q4, e)][r0 + 16mt + r16], e = 0..7
+    floatx4 acc[RK / 16];
     const u16* abase = wt + (4 * q4 + (r16 >> 2)) * PRO_STRIDE + 4 * (r16 & 3);
-#pragma unroll 4
-    for (int mt = 0; mt < PRO_COLS / 16; ++mt) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    constexpr int CPRW = PRO_COLS / 8;   // 16-byte chunks per staged row
 #pragma unroll
-        for (int kd = 0; kd < DH / 32; ++kd) {
-            const u16* pa = abase + kd * 32 * PRO_STRIDE + mt * 16;
-            const u32x2 lo = lds_read_tr16(pa);
-            const u32x2 hi = lds_read_tr16(pa + 16 * PRO_STRIDE);
-            acc = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), qb[kd], acc);
+    for (int qc = 0; qc < 4; ++qc) {
+        // stage columns 128 qc .. 128 qc + 127 of W_UK[j]: 2048 chunks of 16 bytes, 8 per
+        // thread, all eight loads in flight before the first store
+        const u16* wj = w_uk + (size_t)j * DH * RK + qc * PRO_COLS;
+        u32x4 v[DH * CPRW / 256];
+#pragma unroll
+        for (int k = 0; k < DH * CPRW / 256; ++k) {
+            const int c = k * 256 + tid;
+            v[k] = *reinterpret_cast<const u32x4*>(wj + (size_t)(c / CPRW) * RK + (c % CPRW) * 8);
         }
-        if (ok) {
-            u32x2 o;
-            o[0] = pack2h(acc[0] * scale_log2, acc[1] * scale_log2);
-            o[1] = pack2h(acc[2] * scale_log2, acc[3] * scale_log2);
-            *reinterpret_cast<u32x2*>(dst + r0 + mt * 16 + q4 * 4) = o;
+        if (qc > 0) __syncthreads();   // the previous quarter's reads are done
+#pragma unroll
+        for (int k = 0; k < DH * CPRW / 256; ++k) {
+            const int c = k * 256 + tid;
+            *reinterpret_cast<u32x4*>(wt + (c / CPRW) * PRO_STRIDE + (c % CPRW) * 8) = v[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < PRO_COLS / 16; ++mt) {
+            floatx4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kd = 0; kd < DH / 32; ++kd) {
+                const u16* pa = abase + kd * 32 * PRO_STRIDE + mt * 16;
+                const u32x2 lo = lds_read_tr16(pa);
+                const u32x2 hi = lds_read_tr16(pa + 16 * PRO_STRIDE);
+                a = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), qb[kd], a);
+            }
+            acc[qc * (PRO_COLS / 16) + mt] = a;
         }
     }
-    if (ok && blockIdx.z == 0) {
-        // q^R: 64 elements = 8 chunks of 16 bytes; lane group q4 scales chunks q4 and q4 + 4
+
+    // x = q~ * scale * log2(e); the row's largest |x| (over its four lanes) sets 2^E
+    float mx = 0.f;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int off = (q4 + 4 * c) * 8;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(q_rope + qrow * DR + off);
-            u32x4 o;
+    for (int c = 0; c < RK / 16; ++c)
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                o[k] = pack2h(__uint_as_float(v[k] << 16) * scale_log2,
-                              __uint_as_float(v[k] & 0xffff0000u) * scale_log2);
-            *reinterpret_cast<u32x4*>(dst + RK + off) = o;
+        for (int i = 0; i < 4; ++i) {
+            acc[c][i] *= scale_log2;
+            mx = fmaxf(mx, fabsf(acc[c][i]));
         }
+    mx = wave_max16x4(mx);
+    int ex = 0;
+    (void)frexpf(mx, &ex);                        // mx = f 2^ex, f in [0.5, 1); ex = 0 for mx = 0
+    const int E = mx > 0.f ? 14 - ex : 0;         // max |x'| in [2^13, 2^14)
+    const float up = ldexpf(1.f, E), inv = ldexpf(1.f, -E);
+    if (!ok) return;
+#pragma unroll
+    for (int c = 0; c < RK / 16; ++c) {
+        // columns 16 c + 4 q4 + i of the natural latent order (c = 8 qc + mt)
+        const int col = 16 * c + 4 * q4;
+        float xs[4], rs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xs[i] = acc[c][i] * up;
+            const float hv = (float)(_Float16)xs[i];
+            rs[i] = xs[i] - hv;
+            xs[i] = hv;
+        }
+        u32x2 vh, vl;
+        vh[0] = pack2h(xs[0], xs[1]);
+        vh[1] = pack2h(xs[2], xs[3]);
+        vl[0] = pack2h(rs[0], rs[1]);
+        vl[1] = pack2h(rs[2], rs[3]);
+        *reinterpret_cast<u32x2*>(dst + QHI + col * 2) = vh;
+        *reinterpret_cast<u32x2*>(dst + QLO + col * 2) = vl;
     }
+    // q^R: 64 elements; lane group q4 converts elements 16 q4 .. 16 q4 + 15 to fp16
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int off = q4 * 16 + c * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(q_rope + qrow * DR + off);
+        *reinterpret_cast<u32x4*>(dst + QROPE + off * 2) = bf8_to_h8(v);
+    }
+    if (q4 == 0) *reinterpret_cast<float*>(dst + QINV) = inv;
 }
 
 // ---------------------------------------------------------------------------
-// Latent attention.
+// Latent attention: absorb_decode_kernel<NS>.
 //
-// Work split.  A workgroup takes one (context chunk, sequence) pair and NW*16*RG of
-// the s_q*h_q query rows; its NW waves own RG row groups of 16 rows each (the
-// N = 16 side of the 16x16x32 MFMA).
-//   S^T[token][row] = C_tile . q^T      (A = latent rows from LDS, B = queries)
-//   U^T[col][row]  += C_tile^T . P^T    (A = latent columns from LDS, B = P)
-// The softmax state of a row lives in the four lanes l%16 + 16q.  RG = 2 would let
-// every operand read from LDS feed two MFMAs (half the LDS traffic per flop), but u
-// then takes 256 accumulator registers per lane and the wave runs alone on its SIMD,
-// where it cannot hide LDS and MFMA latency: measured on the 128-row flagship shape,
-// 4 waves x 2 row groups ran about 15 % slower than 8 waves x 1, so the launcher uses
-// RG = 1 (two waves per SIMD).
-
-// Data path.  A tile (32 rows x 576, one contiguous span of HBM) goes straight
-// from global memory into LDS with global_load_lds_dwordx4 (lane l of a wave
-// instruction lands at base + 16 l), three buffers deep, so no registers stage it.
-// Buffer slot i (16 bytes) is row i / SROW, column chunk i % SROW of a row-major tile
-// with a 32-byte pad per row; on gfx950 that stride (8 x odd dwords modulo the 64
-// banks) lets both the 16-byte operand reads of 16 rows and the transposing reads
-// of 4 rows x 32 bytes run without bank conflicts.  Pad slots, slots of rows past the
-// chunk and the spare tail slots receive an in-bounds dummy chunk.  Each wave issues
-// exactly NDMA loads per tile and converts its own slots from bf16 to fp16 in place
-// once they have landed (fp16 keeps 10 mantissa bits for the kernel-rounded operands:
-// the absorbed query and P; bf16 data within fp16's range converts exactly).  One
-// barrier per tile publishes the converted tile and retires the buffer the next loads
-// overwrite.  Rows past the chunk hold finite dummy data and get P = 0.
+// Work split.  A workgroup takes one (context chunk, sequence) pair and R = 16 NS of the
+// s_q*h_q query rows.  Its waves are specialised:
+//   - NS score waves: score wave s owns rows 16 s .. 16 s + 15 of the block and the
+//     whole tile's 32 tokens.  It holds that row tile's absorbed queries in registers
+//     (hi, lo and rotary parts: 136 VGPRs), computes
+//       S^T[token][row] = C_tile . q^T   (A = latent rows from LDS, B = queries)
+//     on the 16x16x32 fp16 MFMA, keeps the online softmax state of its rows and writes
+//     P (fp16, in the B-operand layout of the value MFMA) and each row's rescale
+//     factor to LDS.
+//   - 4 value waves: value wave v owns latent columns 128 v .. 128 v + 127 of u for all
+//     R rows (u: 128 VGPRs at R = 64) and computes
+//       U^T[col][row] += C_tile^T . P^T  (A = latent columns from LDS with the gfx950
+//                                          transposing read, B = P from LDS).
+//     Value waves also stream the tiles from HBM and convert them.
+// Waves w and w + 4 share a SIMD, so at R = 64 each SIMD runs one score and one value
+// wave: the score wave's softmax (VALU) runs beside the value wave's MFMAs and the value
+// wave's tile conversion beside the score wave's MFMAs.  Splitting u by columns over
+// value waves and q by rows over score waves keeps both within 256 registers: u for 128
+// rows is 256 KB and q^ (hi + lo) 278 KB, more than a CU's 512 KB register file
+// together, so a workgroup takes 64 rows and the 2 (s_q = 1) or 4 (s_q = 2) row blocks
+// of a (chunk, sequence) pair run as workgroups 8 ids apart, on one XCD, where the
+// second read of every tile is an L2 hit.
+//
+// Pipeline.  Tiles (32 rows x 576, one contiguous span of HBM) go straight from global
+// memory into LDS with global_load_lds_dwordx4 (lane l of a wave instruction lands at
+// base + 16 l), into four buffers.  At step k, after the barrier that published tile k:
+//   score waves:  scores and softmax of tile k (buffer k%4), P and rescale factors to
+//                 the P buffer k%2;
+//   value waves:  issue the loads of tile k+2 (buffer (k+2)%4, last read at step k-1),
+//                 then U += C_{k-1}^T P_{k-1} (buffer (k-1)%4, P buffer (k-1)%2) with the
+//                 in-place bf16 -> fp16 conversion of tile k+1 (buffer (k+1)%4, loaded
+//                 at step k-1) spread over those MFMAs; each value wave converts the
+//                 slots it loaded itself, so it only waits on its own loads;
+// then one barrier.  LDS: 4 tiles of 32 x (576 + 16) fp16 (148 KB) + 2 P buffers.  Rows
+// past the chunk are loaded as copies of the tile's first row (finite data, P = 0).
+// The row stride of 576 + 16 elements (8 x odd dwords modulo the 64 banks) keeps both
+// the 16-byte operand reads of 16 rows and the transposing reads of 4 rows x 32 bytes
+// free of bank conflicts.
+//
+// Scores.  x' = hi + lo (per-row scale 2^E) against the tile's fp16 latent (exact for
+// bf16 data within fp16's range) accumulates 2^E times the latent part of the log2-domain
+// logit; the rotary part multiplies exact fp16 copies of q^R and k_R and is scaled after
+// the MFMA: s = acc * 2^-E + scale log2(e) accr.
 //
 // Softmax.  Online, with a lazily raised reference: exponentials are taken against a
 // per-row reference m (log2 domain) raised only when a tile's maximum exceeds it by more
 // than kLazy, so p = 2^(s - m) <= 2^kLazy, which fp16 P and fp32 sums hold as precisely as
-// values <= 1.  Accumulators are rescaled only when a row that has already accumulated
-// raises its reference, which after the first tiles of a chunk is rare.  Normalisation
-// and log-sum-exp use the same reference, so the result is the exact softmax's.
+// values <= 1.  When a row that has accumulated raises its reference, the value waves
+// multiply its u columns by alpha = 2^(m_old - m_new) before adding the tile; the score
+// wave writes alpha (1 otherwise) beside P.  Normalisation and log-sum-exp use the same
+// reference, so the result is the exact softmax's.
 //
-// Epilogue.  u = U / l is split into two bf16 terms (hi + lo, about 16 significant bits)
-// and multiplied by W_UV[j] on the bf16 MFMA, so the partial written is o (d_h wide).
+// Epilogue.  u / l is split into three bf16 terms (about 24 significant bits); each
+// value wave multiplies its 128 columns by the matching columns of W_UV[j] on the bf16
+// MFMA (a partial sum over those columns), the four partials meet in LDS, and every
+// wave sums and writes a share of the block's R x 128 outputs.
 //
-// Grid.  One-dimensional and XCD-aware: blocks with ids 8 apart run on one XCD, so the
-// nz workgroups of a (chunk, sequence) pair that needs several (s_q*h_q > NW*16*RG)
-// share one L2 and the second read of every tile is an L2 hit.
+// Grid.  One-dimensional and XCD-aware: blocks with ids 8 apart run on one XCD.
 // ---------------------------------------------------------------------------
 constexpr float kLazy = 10.f;
+constexpr int STRIDE = W + 16;                 // LDS row stride in elements
+constexpr int SROW = STRIDE / 8;               // 16-byte slots per LDS row (72 data + 2 pad)
+constexpr int CPR = W / 8;                     // data slots per row
+constexpr int TSLOTS = TT * SROW;              // slots of a tile buffer
+constexpr int NINST = (TSLOTS + 63) / 64;      // 64-lane load instructions per tile (37)
+constexpr int NV = 4;                          // value waves
+constexpr int VI = (NINST + NV - 1) / NV;      // load instructions per value wave (<= 10)
+constexpr int VCOLS = RK / NV;                 // latent columns of u per value wave (128)
+constexpr int NCT = VCOLS / 16;                // 16-wide column tiles per value wave (8)
 
 struct SoftmaxState {
     float m;   // reference (log2 domain), identical in the 4 lanes of a row; -inf before any score
@@ -198,17 +260,6 @@ __device__ __forceinline__ f16x8 softmax_tile(SoftmaxState& st, const float (&sc
     return as_f16x8(u32x4{pack2h(p[0], p[1]), pack2h(p[2], p[3]), pack2h(p[4], p[5]), pack2h(p[6], p[7])});
 }
 
-// A operand of U^T += C^T P^T: lane (q4, r16) needs column col0 + r16 of the tile at the
-// eight tokens 4q4 + e and 16 + 4q4 + e (e = 0..3), the tokens whose scores the lane
-// holds.  Lane m of a 16-lane group addresses row 4q4 + m/4 (then 16 rows further),
-// columns col0 + 4(m%4)..+3; the transposing read hands lane j column col0 + j.
-__device__ __forceinline__ f16x8 gather_col(const u16* lds, int stride, int q4, int r16, int col0) {
-    const u16* p0 = lds + (4 * q4 + (r16 >> 2)) * stride + col0 + 4 * (r16 & 3);
-    const u32x2 lo = lds_read_tr16(p0);
-    const u32x2 hi = lds_read_tr16(p0 + 16 * stride);
-    return as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
 // Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane l's
 // bytes land at LDS byte address lds_base + 16 l; lds_base must be wave-uniform.  It is
 // issued from inline assembly so that the compiler, which cannot tell which LDS bytes
@@ -216,7 +267,7 @@ __device__ __forceinline__ f16x8 gather_col(const u16* lds, int stride, int q4, 
 // callers wait with wait_vmcnt<> before reading the destination.  The compiler does not
 // count these loads, so its own waits on later global loads only over-wait (loads
 // retire in issue order).  The global address is a wave-uniform 64-bit base (SGPRs)
-// plus a 32-bit per-lane byte offset.
+// plus a 32-bit per-lane byte offset.  Lanes outside EXEC write nothing.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
@@ -247,36 +298,29 @@ __device__ __forceinline__ void block_sync() {
     asm volatile("" ::: "memory");
 }
 
-template <int NW, int RG, int CS>
-__global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
-    const u16* __restrict__ qhat, const u16* __restrict__ w_uv,
-    const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
-    int max_ctx, int h_q, int g, int s_q, int chunk, int n_split, int nz, int batch,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
-    constexpr int STRIDE = W + 16;    // LDS row stride in elements
-    constexpr int SROW = STRIDE / 8;  // 16-byte slots per LDS row (72 data + 2 pad)
-    constexpr int CPR = W / 8;        // data slots per row
-    constexpr int KS = W / 32;        // 18 k-steps of the score contraction
-    constexpr int KL = RK / 32;       // 16 of them over the latent part (q~ in registers)
-    constexpr int NU = RK / 16;       // 32 latent column tiles of U^T
-    constexpr int NT = NW * 64;
-    constexpr int TSLOTS = TT * SROW;              // slots of a tile
-    constexpr int NDMA = (TSLOTS + NT - 1) / NT;   // direct loads per wave per tile
-    constexpr int BSLOTS = NDMA * NT;              // slots of a buffer (spare tail included)
-    constexpr int BROWS = (NW / CS) * 16 * RG;     // query rows of a workgroup
-    constexpr int NUW = NU / CS;                   // column tiles of U^T per wave
-    static_assert(NW % CS == 0 && NU % CS == 0 && (CS == 1 || RG == 1), "column split");
-    constexpr int QRS = DR + 16;                   // LDS row stride of the rotary queries
-    // column tile of the U loop at which conversion slot i is read, and written back
-    constexpr auto cv_read = [](int i) { return i * NUW / NDMA; };
-    constexpr auto cv_write = [](int i) { return i * NUW / NDMA + 2 < NUW ? i * NUW / NDMA + 2 : NUW - 1; };
-    // three separately declared buffers: with the tile loop unrolled by three every
-    // access names a fixed buffer, so the compiler can tell that reading one buffer
-    // does not depend on the direct loads still landing in the others
-    __shared__ __attribute__((aligned(16))) u16 buf0[BSLOTS * 8];
-    __shared__ __attribute__((aligned(16))) u16 buf1[BSLOTS * 8];
-    __shared__ __attribute__((aligned(16))) u16 buf2[BSLOTS * 8];
-    __shared__ __attribute__((aligned(16))) u16 qr_lds[BROWS * QRS];
+template <int NS>
+__global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
+    const unsigned char* __restrict__ qrec, const u16* __restrict__ w_uv, const u16* __restrict__ cache,
+    int64_t bstride, const int32_t* __restrict__ ctx_lens, int max_ctx, int h_q, int g, int s_q, int chunk,
+    int n_split, int nz, int batch, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_lse,
+    u16* __restrict__ out, float* __restrict__ lse_out) {
+    constexpr int R = 16 * NS;                     // query rows of a workgroup
+    static_assert(NS >= 1 && NS <= 4, "1..4 score waves");
+    static_assert(NS * 8 * 64 * 16 <= TSLOTS * 16, "a value wave's epilogue partials fit in one tile buffer");
+    // One block of LDS with the small, often-addressed arrays first: ds_read/ds_write
+    // carry a 16-bit immediate offset, so everything below 64 KB is reached from one
+    // per-lane base register; the tile buffers above it need a base per buffer.
+    struct Lds {
+        u16 pbuf[2][NS * 64 * 8];                  // P of the last two tiles (B-operand layout)
+        float abuf[2][R];                          // per-row rescale factor of each P buffer
+        float lfin[R], mfin[R];                    // final softmax sum and reference per row
+        u16 tiles[4][TSLOTS * 8];                  // tile buffers, tile k in buffer k % 4
+    };
+    __shared__ __attribute__((aligned(16))) Lds lds;
+    auto& pbuf = lds.pbuf;
+    auto& abuf = lds.abuf;
+    auto& lfin = lds.lfin;
+    auto& mfin = lds.mfin;
 
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int z = slot % nz;
@@ -284,339 +328,448 @@ __global__ __launch_bounds__(NW * 64) void absorb_decode_kernel(
     if (pair >= n_split * batch) return;           // padding of the last group of 8
     // pair = p * batch + bb with b = (bb + p) mod batch: the sequence index varies fastest
     // across XCDs and chunk p of sequence b runs on XCD (b + p) % 8, so ragged batches
-    // spread evenly (chunk-major numbering would put every sequence's first, always full,
-    // chunk on the same XCD when n_split is a multiple of 8)
+    // spread evenly
     const int p = pair / batch, bb = pair - p * batch;
     const int b = bb + p % batch < batch ? bb + p % batch : bb + p % batch - batch;
     const int L = clampi(ctx_lens[b], 0, max_ctx);
     const int t0 = p * chunk;
-    if (t0 >= L) return;
+    const int RQ = s_q * h_q;
+    const int na = min(NS, (RQ - z * R) / 16);     // active row tiles of the block (RQ % 16 == 0)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q4 = lane >> 4, r16 = lane & 15;
+    const bool direct = n_split == 1;
+
+    if (t0 >= L) {
+        // nothing visible in this chunk; with one chunk per sequence the block writes the
+        // empty result (o = 0, lse = -inf) itself
+        if (direct) {
+            for (int e = tid; e < na * 16 * (DH / 8); e += (NS + NV) * 64) {
+                const int rho = z * R + e / (DH / 8);
+                const int s = rho / h_q, h = rho - (rho / h_q) * h_q;
+                *reinterpret_cast<u32x4*>(out + (((size_t)b * s_q + s) * h_q + h) * DH + (e % (DH / 8)) * 8) =
+                    u32x4{0u, 0u, 0u, 0u};
+                if (lse_out && e % (DH / 8) == 0) lse_out[((size_t)b * s_q + s) * h_q + h] = kNegInf;
+            }
+        }
+        return;
+    }
     const int t1 = min(t0 + chunk, L);
     const int ntiles = (t1 - t0 + TT - 1) / TT;
     // tokens below t_full are visible to every query row and inside the chunk
     const int t_full = min(t1, clampi(L - s_q + 1, 0, L));
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int q4 = lane >> 4, r16 = lane & 15;
-    const int RQ = s_q * h_q;
-    const int hpg = h_q / g;
-    // wave = wslot * CS + part: row slot wslot, latent column part `part` of u
-    const int wslot = wave / CS, part = wave - (wave / CS) * CS;
-    const int rho0 = z * BROWS + wslot * (16 * RG);  // first row of the wave
-    const bool active = rho0 < RQ;
-    int nvis[RG];
-    bool row_ok[RG];
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        const int rho = rho0 + 16 * rg + r16;
-        row_ok[rg] = rho < RQ;
-        const int s = row_ok[rg] ? rho / h_q : 0;
-        nvis[rg] = clampi(L - s_q + s + 1, 0, L);
-    }
-
     const u16* seq = cache + (size_t)b * bstride + (size_t)t0 * W;
-    // byte offset within a tile of the chunk each of this lane's load slots carries
-    // (-1: pad or spare slot)
-    int dma_off[NDMA];
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-        const int sl = (i * NW + wave) * 64 + lane;
-        const int r = sl / SROW, c = sl - r * SROW;
-        dma_off[i] = (sl < TSLOTS && c < CPR) ? (r * W + c * 8) * 2 : -1;
-    }
-    // Issue the direct loads of tile `it` into the buffer at LDS byte address tbuf.
-    // Tiles past the chunk are clamped to its last tile (their buffer is never read), so
-    // every step issues the same number of loads and waits the same way.
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    auto dma_tile = [&](int it, uint32_t tbuf) {
-        it = min(it, ntiles - 1);
-        const u16* tsrc = seq + (size_t)it * TT * W;
-        const int lim = min(TT, t1 - t0 - it * TT) * W * 2;   // rows past the chunk: dummy
-#pragma unroll
-        for (int i = 0; i < NDMA; ++i) {
-            const uint32_t off = (dma_off[i] >= 0 && dma_off[i] < lim) ? (uint32_t)dma_off[i] : 0u;
-            dma16(tsrc, off, tbuf + (uint32_t)((i * NW + wave_s) * 1024));
-        }
-    };
 
-    // absorbed latent queries in registers; the 64 rotary columns of the block's rows in
-    // LDS (read once per tile per row group), published by the first tile barrier
-    f16x8 qv[RG][KL];
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        const u16* qsrc = qhat + ((size_t)b * RQ + (row_ok[rg] ? rho0 + 16 * rg + r16 : 0)) * W + q4 * 8;
-#pragma unroll
-        for (int kk = 0; kk < KL; ++kk) qv[rg][kk] = row_ok[rg] ? ld_f16x8(qsrc + kk * 32) : zero_f16x8();
-    }
-    for (int c = tid; c < BROWS * (DR / 8); c += NT) {
-        const int r = c / (DR / 8), col = c - r * (DR / 8);
-        const int qrow = z * BROWS + r;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (qrow < RQ) v = *reinterpret_cast<const u32x4*>(qhat + ((size_t)b * RQ + qrow) * W + RK + col * 8);
-        *reinterpret_cast<u32x4*>(qr_lds + r * QRS + col * 8) = v;
-    }
+    auto bufp = [&](int i) -> u16* { return lds.tiles[i & 3]; };   // buffer of tile i
 
-    floatx4 uacc[RG][NUW];
+    // The two roles run separate code with the same sequence of barriers (one before the
+    // tile loop, one per step, one in the epilogue), so that the compiler
+    // never holds the score waves' queries and the value waves' accumulators at once.
+    if (wave < NS) {
+        // ============================== score wave: row tile sw
+        const int sw = wave;
+        const bool active = sw < na;
+        f16x8 qhi[RK / 32], qlo[RK / 32], qro[DR / 32];
+        float qinv = 0.f;
+        int nvis = 0;
+        SoftmaxState st{kNegInf, 0.f};
+        if (active) {
+            const int rho = z * R + 16 * sw + r16;
+            const unsigned char* rec = qrec + ((size_t)b * RQ + rho) * QREC;
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-        for (int n = 0; n < NUW; ++n) uacc[rg][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-    SoftmaxState st[RG];
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) st[rg] = SoftmaxState{kNegInf, 0.f};
-
-    // One tile: (barrier) start the loads of tile it+2, compute tile it, and while the
-    // U MFMAs run convert this wave's slots of tile it+1 (its loads were issued one step
-    // earlier).  The barrier marks tile it converted by every wave and tile it-1, whose
-    // buffer the new loads reuse, consumed by every wave.  A wave whose rows all lie
-    // past s_q*h_q computes on zero queries and discards the result: every wave runs
-    // the same straight-line step, so the conversion can interleave with the MFMAs.
-    auto step = [&](int it, const u16* lds, uint32_t dma_buf, u16* next_lds) {
-        const int tb = t0 + it * TT;
-        block_sync();
-        dma_tile(it + 2, dma_buf);
-        f16x8 pb[RG];
-        {
-            floatx4 acc[RG][2];
-#pragma unroll
-            for (int rg = 0; rg < RG; ++rg) acc[rg][0] = acc[rg][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-            const u16* arow = lds + r16 * STRIDE + q4 * 8;
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const f16x8 a0 = ld_f16x8(arow + kk * 32);
-                const f16x8 a1 = ld_f16x8(arow + 16 * STRIDE + kk * 32);
-#pragma unroll
-                for (int rg = 0; rg < RG; ++rg) {
-                    const f16x8 bq = kk < KL ? qv[rg][kk]
-                                             : ld_f16x8(qr_lds + (wslot * 16 * RG + 16 * rg + r16) * QRS +
-                                                        (kk - KL) * 32 + q4 * 8);
-                    acc[rg][0] = mfma16h(a0, bq, acc[rg][0]);
-                    acc[rg][1] = mfma16h(a1, bq, acc[rg][1]);
-                }
-                // bound how far the scheduler hoists operand reads (register pressure)
-                if (kk % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+            for (int kk = 0; kk < RK / 32; ++kk) {
+                qhi[kk] = ld_f16x8(reinterpret_cast<const u16*>(rec + QHI) + kk * 32 + q4 * 8);
+                qlo[kk] = ld_f16x8(reinterpret_cast<const u16*>(rec + QLO) + kk * 32 + q4 * 8);
             }
 #pragma unroll
-            for (int rg = 0; rg < RG; ++rg) {
+            for (int kr = 0; kr < DR / 32; ++kr)
+                qro[kr] = ld_f16x8(reinterpret_cast<const u16*>(rec + QROPE) + kr * 32 + q4 * 8);
+            qinv = *reinterpret_cast<const float*>(rec + QINV);
+            nvis = clampi(L - s_q + rho / h_q + 1, 0, L);
+        }
+        auto sstep = [&](int k) {
+            if (active && k < ntiles) {
+                const u16* const tile = bufp(k);
+                u16* const pw = pbuf[k & 1];
+                float* const aw = abuf[k & 1];
+                const int tb = t0 + k * TT;
+                floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, accr0 = acc0, accr1 = acc0;
+                const u16* arow = tile + r16 * STRIDE + q4 * 8;
+                // k-step j = 0..17 reads columns 32 j .. 32 j + 31 (latent for j < 16, rotary
+                // after); its operand reads are issued PF steps ahead of its MFMAs, which the
+                // scheduling barriers keep in this order
+                constexpr int KS = W / 32, PF = 3;
+                f16x8 ra0[PF + 1], ra1[PF + 1];
+#pragma unroll
+                for (int j = 0; j < PF; ++j) {
+                    ra0[j] = ld_f16x8(arow + j * 32);
+                    ra1[j] = ld_f16x8(arow + 16 * STRIDE + j * 32);
+                }
+#pragma unroll
+                for (int j = 0; j < KS; ++j) {
+                    if (j + PF < KS) {
+                        ra0[(j + PF) % (PF + 1)] = ld_f16x8(arow + (j + PF) * 32);
+                        ra1[(j + PF) % (PF + 1)] = ld_f16x8(arow + 16 * STRIDE + (j + PF) * 32);
+                    }
+                    const f16x8 a0 = ra0[j % (PF + 1)], a1 = ra1[j % (PF + 1)];
+                    if (j < RK / 32) {
+                        acc0 = mfma16h(a0, qhi[j], acc0);
+                        acc1 = mfma16h(a1, qhi[j], acc1);
+                        acc0 = mfma16h(a0, qlo[j], acc0);
+                        acc1 = mfma16h(a1, qlo[j], acc1);
+                    } else {
+                        accr0 = mfma16h(a0, qro[j - RK / 32], accr0);
+                        accr1 = mfma16h(a1, qro[j - RK / 32], accr1);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 float sc[8];
-                if (tb + TT <= t_full) {
 #pragma unroll
-                    for (int th = 0; th < 2; ++th)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) sc[th * 4 + i] = acc[rg][th][i];
-                } else {
+                for (int i = 0; i < 4; ++i) {
+                    sc[i] = fmaf(accr0[i], scale_log2, acc0[i] * qinv);
+                    sc[4 + i] = fmaf(accr1[i], scale_log2, acc1[i] * qinv);
+                }
+                if (tb + TT > t_full) {
 #pragma unroll
                     for (int th = 0; th < 2; ++th)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int t = tb + th * 16 + q4 * 4 + i;
-                            sc[th * 4 + i] = (row_ok[rg] && t < t1 && t < nvis[rg]) ? acc[rg][th][i] : kNegInf;
+                            if (!(t < t1 && t < nvis)) sc[th * 4 + i] = kNegInf;
                         }
                 }
                 bool need;
                 float alpha;
-                pb[rg] = softmax_tile(st[rg], sc, need, alpha);
-                if (__builtin_expect(__any(need), 0)) {
-                    // rare: kept as a real branch so the accumulators are not touched on
-                    // the common path
-                    asm volatile("" ::: "memory");
-#pragma unroll
-                    for (int n = 0; n < NUW; ++n) uacc[rg][n] *= alpha;
-                }
-            }
-        }
-        wait_vmcnt<NDMA>();   // this wave's loads of tile it+1 have landed
-        // U MFMAs, with the conversion of this wave's NDMA slots of tile it+1 spread over
-        // them: slot i is read at column tile cv_read(i) and written back converted two
-        // column tiles later, so only a few slots are held in registers at a time
-        u32x4 cv[NDMA];
-#pragma unroll
-        for (int n = 0; n < NUW; ++n) {
-#pragma unroll
-            for (int i = 0; i < NDMA; ++i)
-                if (cv_read(i) == n)
-                    cv[i] = *reinterpret_cast<const u32x4*>(next_lds + ((i * NW + wave) * 64 + lane) * 8);
-            const f16x8 a = gather_col(lds, STRIDE, q4, r16, 16 * (part * NUW + n));
-#pragma unroll
-            for (int rg = 0; rg < RG; ++rg) uacc[rg][n] = mfma16h(a, pb[rg], uacc[rg][n]);
-#pragma unroll
-            for (int i = 0; i < NDMA; ++i)
-                if (cv_write(i) == n)
-                    *reinterpret_cast<u32x4*>(next_lds + ((i * NW + wave) * 64 + lane) * 8) = bf8_to_h8(cv[i]);
-            if (n % 8 == 7) __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    const uint32_t a0 = lds_addr(buf0), a1 = lds_addr(buf1), a2 = lds_addr(buf2);
-    dma_tile(0, a0);
-    dma_tile(1, a1);
-    wait_vmcnt<NDMA>();
-    {
-#pragma unroll
-        for (int i = 0; i < NDMA; ++i) {
-            u16* ptr = buf0 + ((i * NW + wave) * 64 + lane) * 8;
-            *reinterpret_cast<u32x4*>(ptr) = bf8_to_h8(*reinterpret_cast<const u32x4*>(ptr));
-        }
-    }
-    for (int it = 0; it < ntiles; it += 3) {
-        step(it, buf0, a2, buf1);
-        if (it + 1 < ntiles) step(it + 1, buf1, a0, buf2);
-        if (it + 2 < ntiles) step(it + 2, buf2, a1, buf0);
-    }
-    // no direct load may still be writing this workgroup's LDS when it ends
-    wait_vmcnt<0>();
-    if constexpr (CS == 1) {
-        if (!active) return;
-
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            const int rho = rho0 + 16 * rg + r16;
-            const int s = row_ok[rg] ? rho / h_q : 0;
-            const int h = row_ok[rg] ? rho - s * h_q : 0;
-            const float l = wave_sum16x4(st[rg].l);
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            // U^T as the B operand of o^T = W_UV[j] U^T: k-step ks covers latent columns
-            // 32ks + (token slot order of P), which are uacc[2ks + e/4][e%4] of this lane
-            bf16x8 ub[RK / 32], ul[RK / 32];
-#pragma unroll
-            for (int ks = 0; ks < RK / 32; ++ks) {
-                u32x4 vh, vl;
-#pragma unroll
-                for (int hh = 0; hh < 4; ++hh) {
-                    const floatx4& src = uacc[rg][2 * ks + (hh >> 1)];
-                    const float a = src[2 * (hh & 1)] * inv, c = src[2 * (hh & 1) + 1] * inv;
-                    const u16 ah = f2bf(a), ch = f2bf(c);
-                    vh[hh] = pack2(ah, ch);
-                    vl[hh] = pack2f(a - bf2f(ah), c - bf2f(ch));
-                }
-                ub[ks] = as_bf16x8(vh);
-                ul[ks] = as_bf16x8(vl);
-            }
-            const int jrow = h / hpg;
-            const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
-            // groups of the row group's 16 rows (they never straddle a query token: h_q % 16 == 0)
-            const int first = rho0 + 16 * rg;
-            const int last = min(first + 15, RQ - 1);
-            if (first > last) continue;
-            const int jlo = (first % h_q) / hpg, jhi = (last % h_q) / hpg;
-            for (int jj = jlo; jj <= jhi; ++jj) {
-                const u16* wj = w_uv + (size_t)jj * DH * RK;
-#pragma unroll 2
-                for (int mt = 0; mt < DH / 16; ++mt) {
-                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                    const u16* wrow = wj + (size_t)(mt * 16 + r16) * RK + q4 * 4;
-#pragma unroll
-                    for (int ks = 0; ks < RK / 32; ++ks) {
-                        const u32x2 lo = *reinterpret_cast<const u32x2*>(wrow + ks * 32);
-                        const u32x2 hi = *reinterpret_cast<const u32x2*>(wrow + ks * 32 + 16);
-                        const bf16x8 wa = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-                        acc = mfma16(wa, ub[ks], acc);
-                        acc = mfma16(wa, ul[ks], acc);
+                const f16x8 pb = softmax_tile(st, sc, need, alpha);
+                *reinterpret_cast<u32x4*>(pw + (sw * 64 + lane) * 8) = __builtin_bit_cast(u32x4, pb);
+                if (q4 == 0) aw[16 * sw + r16] = need ? alpha : 1.f;
+                if (k == ntiles - 1) {
+                    const float l = wave_sum16x4(st.l);
+                    if (q4 == 0) {
+                        lfin[16 * sw + r16] = l;
+                        mfin[16 * sw + r16] = st.m;
                     }
-                    if (row_ok[rg] && jrow == jj) *reinterpret_cast<floatx4*>(part_o + prow * DH + mt * 16 + q4 * 4) = acc;
                 }
             }
-            if (row_ok[rg] && q4 == 0) part_lse[prow] = l > 0.f ? (st[rg].m + __log2f(l)) * kLn2 : kNegInf;
+            block_sync();
+        };
+        if (!active) {
+            // a row tile past s_q*h_q: P = 0 and rescale factor 1 in both P buffers, so the
+            // value waves' loop needs no per-tile condition; final sum 0
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                *reinterpret_cast<u32x4*>(pbuf[j] + (sw * 64 + lane) * 8) = u32x4{0u, 0u, 0u, 0u};
+                if (q4 == 0) abuf[j][16 * sw + r16] = 1.f;
+            }
+            if (q4 == 0) {
+                lfin[16 * sw + r16] = 0.f;
+                mfin[16 * sw + r16] = kNegInf;
+            }
+        }
+        block_sync();   // tile 0 converted
+#pragma unroll 1
+        for (int k = 0; k <= ntiles; ++k) sstep(k);
+        block_sync();   // value waves' epilogue partials written
+        if (active && q4 == 0) {
+            const int rho = z * R + 16 * sw + r16;
+            const int s = rho / h_q, h = rho - (rho / h_q) * h_q;
+            const float l = lfin[16 * sw + r16];
+            const float v = l > 0.f ? (mfin[16 * sw + r16] + __log2f(l)) * kLn2 : kNegInf;
+            if (direct) {
+                if (lse_out) lse_out[((size_t)b * s_q + s) * h_q + h] = v;
+            } else {
+                part_lse[((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h] = v;
+            }
         }
     } else {
-        // Column-split epilogue (one row group per wave).  The wave holds u for its 16 rows
-        // over latent columns [part * RK / CS, (part + 1) * RK / CS), so its W_UV product
-        // is a partial sum over those columns; the CS partials of a row slot meet in LDS
-        // (the tile buffers, free once every wave has passed the barrier below) and each
-        // wave of the slot sums and writes every CS-th 16-wide block of d_h.
-        block_sync();
-        constexpr int KSW = NUW / 2;   // k-steps of the wave's columns
-        const int rho = rho0 + r16;
-        const bool rok = row_ok[0];
-        const int s = rok ? rho / h_q : 0;
-        const int h = rok ? rho - s * h_q : 0;
-        const float l = wave_sum16x4(st[0].l);
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        bf16x8 ub[KSW], ul[KSW];
+        // ============================== value wave: latent columns VCOLS vw .. + VCOLS - 1
+        const int vw = wave - NS;
+        floatx4 uacc[NCT][NS];
 #pragma unroll
-        for (int ks = 0; ks < KSW; ++ks) {
-            u32x4 vh, vl;
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int hh = 0; hh < 4; ++hh) {
-                const floatx4& src = uacc[0][2 * ks + (hh >> 1)];
-                const float x = src[2 * (hh & 1)] * inv, y = src[2 * (hh & 1) + 1] * inv;
-                const u16 xh = f2bf(x), yh = f2bf(y);
-                vh[hh] = pack2(xh, yh);
-                vl[hh] = pack2f(x - bf2f(xh), y - bf2f(yh));
-            }
-            ub[ks] = as_bf16x8(vh);
-            ul[ks] = as_bf16x8(vl);
+            for (int rt = 0; rt < NS; ++rt) uacc[ct][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // Byte offset within a tile of the chunk that each of this lane's load slots carries,
+        // two 16-bit offsets per register (a tile is 36,864 bytes).  The 37 instructions of a
+        // tile cover its 2368 slots exactly; the two pad slots of an LDS row load that row's
+        // first 16 bytes (a line the row's first slot loads anyway) and are never read, so
+        // every slot loads and converts without a condition.
+        static_assert(NINST * 64 == TSLOTS, "load instructions cover the tile exactly");
+        uint32_t dma_off2[(VI + 1) / 2];
+#pragma unroll
+        for (int i = 0; i < (VI + 1) / 2; ++i) dma_off2[i] = 0;
+#pragma unroll
+        for (int i = 0; i < VI; ++i) {
+            const int sl = (vw + NV * i) * 64 + lane;
+            const int r = sl / SROW, c = sl - (sl / SROW) * SROW;
+            const uint32_t o = sl < TSLOTS ? (uint32_t)((r * W + (c < CPR ? c : 0) * 8) * 2) : 0u;
+            dma_off2[i / 2] |= o << (16 * (i & 1));
         }
-        const int jrow = h / hpg;
-        floatx4 ores[DH / 16];
+        auto slot_off = [&](int i) -> uint32_t { return (dma_off2[i / 2] >> (16 * (i & 1))) & 0xffffu; };
+        // The offsets are loop-invariant; left visible, the compiler unpacks (and for the
+        // tail, reduces) all of them before the tile loop and runs out of registers.
+        // Re-declaring them opaque at each step keeps them packed.
+        auto opaque_offsets = [&]() {
 #pragma unroll
-        for (int mt = 0; mt < DH / 16; ++mt) ores[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (active) {
-            const int first = rho0;
-            const int last = min(first + 15, RQ - 1);
-            const int jlo = (first % h_q) / hpg, jhi = (last % h_q) / hpg;
+            for (int i = 0; i < (VI + 1) / 2; ++i) asm volatile("" : "+v"(dma_off2[i]));
+        };
+        const int vslot = vw * 64 + lane;   // slot of instruction 0; instruction i adds 4 * 64 i
+        const bool full = vw < NINST % NV || NINST % NV == 0;   // this wave issues VI loads per tile (else VI - 1)
+        // Direct loads of tile `it` into the buffer at LDS byte address tbuf: instruction i of
+        // value wave vw fills slots (vw + 4 i) * 64 .. + 63.  Rows past the chunk load the
+        // tile's first row instead.
+        auto dma_tile = [&](int it, uint32_t tbuf) {
+            const u16* tsrc = seq + (size_t)it * TT * W;
+            const int rows = t1 - t0 - it * TT;
+            if (rows >= TT) {
+#pragma unroll
+                for (int i = 0; i < VI; ++i)
+                    if (i < VI - 1 || full) dma16(tsrc, slot_off(i), tbuf + (uint32_t)((vw + NV * i) * 1024));
+            } else {
+                const uint32_t lim = (uint32_t)(rows * W * 2);
+#pragma unroll
+                for (int i = 0; i < VI; ++i) {
+                    const uint32_t o = slot_off(i);
+                    if (i < VI - 1 || full)
+                        dma16(tsrc, o < lim ? o : o % (uint32_t)(W * 2), tbuf + (uint32_t)((vw + NV * i) * 1024));
+                }
+            }
+        };
+        // wait until this wave's loads of the older tile have landed, leaving the loads of
+        // the newer tile (issued after them, when `newer`) in flight
+        auto wait_own = [&](bool newer) {
+            if (!newer) {
+                wait_vmcnt<0>();
+            } else if (full) {
+                wait_vmcnt<VI>();
+            } else {
+                wait_vmcnt<VI - 1>();
+            }
+        };
+        // tb: the tile buffer already offset to this lane's first slot (tb + vslot * 8)
+        auto convert_slot = [&](u16* tb, int i) {
+            if (i < VI - 1 || full) {
+                u16* ptr = tb + i * NV * 64 * 8;
+                *reinterpret_cast<u32x4*>(ptr) = bf8_to_h8(*reinterpret_cast<const u32x4*>(ptr));
+            }
+        };
+        // lane offset of the transposing reads of column tile 0 of this wave's columns
+        const int goff = (4 * q4 + (r16 >> 2)) * STRIDE + VCOLS * vw + 4 * (r16 & 3);
+        // Step k >= 1 of the pipeline.  The conversion of tile k+1 runs unconditionally: when
+        // there is no tile k+1 its buffer (that of tile k-3) is free and holds data nobody
+        // reads, so the value MFMAs run as one straight sequence.
+        auto vstep = [&](int k) {
+            opaque_offsets();
+            // per-lane bases, opaque per step: the addresses derived from them are then
+            // recomputed in each step (one add each) instead of being hoisted out of the
+            // loop for all four buffers and held in registers
+            int vs = vslot, go = goff, ln = lane;
+            asm volatile("" : "+v"(vs), "+v"(go), "+v"(ln));
+            u16* const cbase = bufp(k + 1) + vs * 8;   // tile k+1 (converted this step)
+            const u16* const bval = bufp(k + 3);       // tile k-1
+            const u16* const pr = pbuf[(k + 1) & 1];
+            const float* const ar = abuf[(k + 1) & 1];
+            const bool more = k + 2 < ntiles;
+            if (more) dma_tile(k + 2, lds_addr(bufp(k + 2)));
+            // rescale rows whose reference rose at tile k-1 (rare)
+            float al[NS];
+#pragma unroll
+            for (int rt = 0; rt < NS; ++rt) al[rt] = ar[16 * rt + (ln & 15)];
+            bool any = false;
+#pragma unroll
+            for (int rt = 0; rt < NS; ++rt) any = any || al[rt] != 1.f;
+            if (__builtin_expect(__any(any), 0)) {
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int rt = 0; rt < NS; ++rt) uacc[ct][rt] *= al[rt];
+            }
+            f16x8 pv[NS];
+#pragma unroll
+            for (int rt = 0; rt < NS; ++rt) pv[rt] = ld_f16x8(pr + (rt * 64 + ln) * 8);
+            // A operands (transposing reads of a 16-column tile) are read two column tiles
+            // ahead of their MFMAs
+            constexpr int PV = 2;
+            u32x4 ra[PV + 1];
+            auto read_a = [&](int ct) -> u32x4 {
+                const u16* p0 = bval + go + 16 * ct;
+                const u32x2 lo = lds_read_tr16(p0);
+                const u32x2 hi = lds_read_tr16(p0 + 16 * STRIDE);
+                return u32x4{lo[0], lo[1], hi[0], hi[1]};
+            };
+#pragma unroll
+            for (int c = 0; c < PV; ++c) ra[c] = read_a(c);
+            // this wave's slots of tile k+1: all read once their loads have landed, then
+            // converted and written back one or two per column tile
+            wait_own(more);
+            u32x4 cv[VI];
+#pragma unroll
+            for (int i = 0; i < VI; ++i)
+                if (i < VI - 1 || full) cv[i] = *reinterpret_cast<const u32x4*>(cbase + i * NV * 64 * 8);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                if (ct + PV < NCT) ra[(ct + PV) % (PV + 1)] = read_a(ct + PV);
+                const f16x8 a = as_f16x8(ra[ct % (PV + 1)]);
+#pragma unroll
+                for (int rt = 0; rt < NS; ++rt) uacc[ct][rt] = mfma16h(a, pv[rt], uacc[ct][rt]);
+#pragma unroll
+                for (int i = 0; i < VI; ++i)
+                    if (i * NCT / VI == ct && (i < VI - 1 || full))
+                        *reinterpret_cast<u32x4*>(cbase + i * NV * 64 * 8) = bf8_to_h8(cv[i]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            block_sync();
+        };
+        // prologue of the pipeline: tiles 0 and 1 loaded, tile 0 converted; then step 0
+        // (loads of tile 2, conversion of tile 1)
+        dma_tile(0, lds_addr(bufp(0)));
+        const bool two = ntiles > 1;
+        if (two) dma_tile(1, lds_addr(bufp(1)));
+        wait_own(two);
+#pragma unroll
+        for (int i = 0; i < VI; ++i) convert_slot(bufp(0) + vslot * 8, i);
+        block_sync();
+        {
+            const bool more = 2 < ntiles;
+            if (more) dma_tile(2, lds_addr(bufp(2)));
+            wait_own(more);
+#pragma unroll
+            for (int i = 0; i < VI; ++i) convert_slot(bufp(1) + vslot * 8, i);
+            block_sync();
+        }
+#pragma unroll 1
+        for (int k = 1; k <= ntiles; ++k) vstep(k);
+        // no direct load may still be writing this workgroup's LDS
+        wait_vmcnt<0>();
+
+        // ---- epilogue: o^T = W_UV[j] (u / l)^T, a partial sum over this wave's columns.
+        // u goes to tile buffer vw first (free: the last step's barrier retired every tile),
+        // as 8 KB per row tile; each row tile is then read back, multiplied, and its partial
+        // (also 8 KB) written over it.  Storing u at once ends the accumulators' lives at
+        // the loop exit, so the epilogue never holds them next to its own registers.
+        float* red = reinterpret_cast<float*>(bufp(vw));
+#pragma unroll
+        for (int rt = 0; rt < NS; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                *reinterpret_cast<floatx4*>(red + (((rt * 8) + ct) * 64 + lane) * 4) = uacc[ct][rt];
+        const int hpg = h_q / g;
+#pragma unroll 1
+        for (int rt = 0; rt < na; ++rt) {
+            float* blk = red + rt * 8 * 64 * 4;
+            const float l = lfin[16 * rt + r16];
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            // U^T as the B operand of o^T = W_UV[j] U^T: k-step ks covers latent columns
+            // VCOLS vw + 32 ks + (token slot order of P), which are column tiles 2ks and
+            // 2ks + 1 of u, element e%4.  u / l is carried as three bf16 terms (about 24
+            // significant bits): o = W_UV u can cancel to values far below |u| (a one-hot
+            // softmax over latent rows of magnitude 1e4 leaves u = c_t), and two terms
+            // (16 bits) would then miss the 2e-3 absolute bound.
+            bf16x8 ub[NCT / 2], um[NCT / 2], ul[NCT / 2];
+#pragma unroll
+            for (int ks = 0; ks < NCT / 2; ++ks) {
+                const floatx4 c0 = *reinterpret_cast<const floatx4*>(blk + ((2 * ks) * 64 + lane) * 4);
+                const floatx4 c1 = *reinterpret_cast<const floatx4*>(blk + ((2 * ks + 1) * 64 + lane) * 4);
+                u32x4 vh, vm, vl;
+#pragma unroll
+                for (int hh = 0; hh < 4; ++hh) {
+                    const floatx4& src = (hh >> 1) ? c1 : c0;
+                    const float x = src[2 * (hh & 1)] * inv, y = src[2 * (hh & 1) + 1] * inv;
+                    const u16 xh = f2bf(x), yh = f2bf(y);
+                    const float xr = x - bf2f(xh), yr = y - bf2f(yh);
+                    const u16 xm = f2bf(xr), ym = f2bf(yr);
+                    vh[hh] = pack2(xh, yh);
+                    vm[hh] = pack2(xm, ym);
+                    vl[hh] = pack2f(xr - bf2f(xm), yr - bf2f(ym));
+                }
+                ub[ks] = as_bf16x8(vh);
+                um[ks] = as_bf16x8(vm);
+                ul[ks] = as_bf16x8(vl);
+            }
+            const int rho = z * R + 16 * rt + r16;
+            const int jrow = (rho % h_q) / hpg;
+            const int first = z * R + 16 * rt;
+            const int jlo = (first % h_q) / hpg, jhi = ((first % h_q) + 15) / hpg;
+            // each lane's row belongs to exactly one group jj of the row tile; its partial
+            // is written in that group's pass
             for (int jj = jlo; jj <= jhi; ++jj) {
-                const u16* wj = w_uv + (size_t)jj * DH * RK + part * (RK / CS);
+                // all of the group's weight operands for this wave's columns are loaded
+                // before the first MFMA (one round trip to L2 per row tile and group)
+                const u16* wrow = w_uv + (size_t)jj * DH * RK + VCOLS * vw + (size_t)r16 * RK + q4 * 4;
+                u32x4 wa[DH / 16][NCT / 2];
 #pragma unroll
-                for (int mt = 0; mt < DH / 16; ++mt) {
-                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                    const u16* wrow = wj + (size_t)(mt * 16 + r16) * RK + q4 * 4;
+                for (int dt = 0; dt < DH / 16; ++dt)
 #pragma unroll
-                    for (int ks = 0; ks < KSW; ++ks) {
-                        const u32x2 lo = *reinterpret_cast<const u32x2*>(wrow + ks * 32);
-                        const u32x2 hi = *reinterpret_cast<const u32x2*>(wrow + ks * 32 + 16);
-                        const bf16x8 wa = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-                        acc = mfma16(wa, ub[ks], acc);
-                        acc = mfma16(wa, ul[ks], acc);
+                    for (int ks = 0; ks < NCT / 2; ++ks) {
+                        const u16* pw = wrow + (size_t)dt * 16 * RK + ks * 32;
+                        const u32x2 lo = *reinterpret_cast<const u32x2*>(pw);
+                        const u32x2 hi = *reinterpret_cast<const u32x2*>(pw + 16);
+                        wa[dt][ks] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                     }
-                    if (jrow == jj) ores[mt] = acc;
+#pragma unroll
+                for (int dt = 0; dt < DH / 16; ++dt) {
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < NCT / 2; ++ks) {
+                        acc = mfma16(as_bf16x8(wa[dt][ks]), ub[ks], acc);
+                        acc = mfma16(as_bf16x8(wa[dt][ks]), um[ks], acc);
+                        acc = mfma16(as_bf16x8(wa[dt][ks]), ul[ks], acc);
+                    }
+                    if (jrow == jj) *reinterpret_cast<floatx4*>(blk + (dt * 64 + lane) * 4) = acc;
                 }
             }
         }
-        // partial of wave w, block mt: buffer mt / 4, floatx4 slot (w * 4 + mt % 4) * 64 + lane
-        float* red0 = reinterpret_cast<float*>(buf0);
-        float* red1 = reinterpret_cast<float*>(buf1);
-        static_assert(NW * 4 * 64 * 16 <= (int)sizeof(buf0), "partials fit in a tile buffer");
-#pragma unroll
-        for (int mt = 0; mt < DH / 16; ++mt)
-            *reinterpret_cast<floatx4*>((mt < 4 ? red0 : red1) + ((wave * 4 + (mt & 3)) * 64 + lane) * 4) = ores[mt];
         block_sync();
-        if (active && rok) {
-            const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
-            for (int mt = part; mt < DH / 16; mt += CS) {
-                floatx4 sum = {0.f, 0.f, 0.f, 0.f};
+    }
+    // sum the four partials: (row tile, d tile) pairs are dealt round-robin over all waves
+    for (int pr_ = wave; pr_ < na * 8; pr_ += NS + NV) {
+        const int rt = pr_ >> 3, dt = pr_ & 7;
+        floatx4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c = 0; c < CS; ++c)
-                    sum += *reinterpret_cast<const floatx4*>((mt < 4 ? red0 : red1) +
-                                                             (((wslot * CS + c) * 4 + (mt & 3)) * 64 + lane) * 4);
-                *reinterpret_cast<floatx4*>(part_o + prow * DH + mt * 16 + q4 * 4) = sum;
-            }
-            if (part == 0 && q4 == 0) part_lse[prow] = l > 0.f ? (st[0].m + __log2f(l)) * kLn2 : kNegInf;
+        for (int v = 0; v < NV; ++v)
+            sum += *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(bufp(v)) +
+                                                     (((rt * 8) + dt) * 64 + lane) * 4);
+        const int rho = z * R + 16 * rt + r16;
+        const int s = rho / h_q, h = rho - (rho / h_q) * h_q;
+        const int d0 = dt * 16 + q4 * 4;
+        if (direct) {
+            u32x2 o;
+            o[0] = pack2f(sum[0], sum[1]);
+            o[1] = pack2f(sum[2], sum[3]);
+            *reinterpret_cast<u32x2*>(out + (((size_t)b * s_q + s) * h_q + h) * DH + d0) = o;
+        } else {
+            const size_t prow = ((size_t)p * batch * s_q + (size_t)b * s_q + s) * h_q + h;
+            *reinterpret_cast<floatx4*>(part_o + prow * DH + d0) = sum;
         }
     }
 }
 
-template <int NW, int RG, int CS>
+template <int NS>
 hipError_t launch_absorb_t(const DecodeArgs& a, int nz, hipStream_t st) {
     const int pairs = a.n_split * a.batch;
     dim3 grid(((pairs + 7) / 8) * 8 * nz);
-    hipLaunchKernelGGL((absorb_decode_kernel<NW, RG, CS>), grid, dim3(NW * 64), 0, st, (const u16*)a.qhat,
-                       (const u16*)a.w_uv, (const u16*)a.cache, a.bstride, a.ctx_lens, a.max_ctx, a.h_q, a.g,
-                       a.s_q, a.chunk, a.n_split, nz, a.batch, a.part_o, a.part_lse);
+    hipLaunchKernelGGL((absorb_decode_kernel<NS>), grid, dim3((NS + NV) * 64), 0, st,
+                       (const unsigned char*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride,
+                       a.ctx_lens, a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.n_split, nz, a.batch,
+                       a.scale * kLog2e, a.part_o, a.part_lse, (u16*)a.out, a.lse);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int absorb_block_rows(int query_rows) { return query_rows <= 32 ? 32 : (query_rows <= 64 ? 64 : 128); }
+int absorb_block_rows(int query_rows) { return query_rows < 64 ? query_rows : 64; }
+
+size_t absorb_qrec_bytes() { return QREC; }
 
 hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st) {
     const int hpg = a.h_q / a.g;
     const int rows_per_group = a.batch * a.s_q * hpg;
-    dim3 pgrid((rows_per_group + 63) / 64, a.g, RK / PRO_COLS);
+    dim3 pgrid((rows_per_group + 63) / 64, a.g);
     hipLaunchKernelGGL(absorb_prologue_kernel, pgrid, dim3(256), 0, st,
-                       (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.w_uk, (u16*)a.qhat,
+                       (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.w_uk, (unsigned char*)a.qhat,
                        a.batch, a.h_q, a.g, a.s_q, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -625,12 +778,11 @@ hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st) {
     const int nz = (RQ + rows - 1) / rows;
     e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;
-    if (rows == 32) {
-        e = launch_absorb_t<8, 1, 4>(a, nz, st);
-    } else if (rows == 64) {
-        e = launch_absorb_t<8, 1, 2>(a, nz, st);
-    } else {
-        e = launch_absorb_t<8, 1, 1>(a, nz, st);
+    switch (rows / 16) {
+        case 1: e = launch_absorb_t<1>(a, nz, st); break;
+        case 2: e = launch_absorb_t<2>(a, nz, st); break;
+        case 3: e = launch_absorb_t<3>(a, nz, st); break;
+        default: e = launch_absorb_t<4>(a, nz, st); break;
     }
     if (e != hipSuccess) return e;
     return record_if(a.ev_after, st);

@@ -253,20 +253,22 @@ def test_plan_lens_long_ragged_context(lib):
     rng = np.random.default_rng(5)
     lens = rng.integers(65536, 131073, size=16).astype(np.int32)
     cap = int(lens.max())
-    for path in (gqla.ABSORB, gqla.GQA):
+    for path, blocks in ((gqla.ABSORB, 2), (gqla.GQA, 1)):
+        # absorb workgroups hold 64 of the 128 query rows: two per (chunk, sequence)
         w, n, c = gqla.plan_splits_lens(FLAG, path, lens, cap)
         assert w > 0 and (n, c) == gqla.plan_splits(FLAG, path, 16, cap, w)
-        units = sum((int(L) + c - 1) // c for L in lens)
+        units = blocks * sum((int(L) + c - 1) // c for L in lens)
         assert units <= 256 and n * c >= cap
         assert c > gqla.plan_splits(FLAG, path, 16, cap, 0)[1]
 
 
 def test_plan_lens_uniform_flagship(lib):
-    # 128 sequences of 8192 tokens on 256 compute units: two chunks each, one per CU
+    # 128 sequences of 8192 tokens on 256 compute units, one workgroup per CU: GQA cuts
+    # two chunks per sequence; absorb keeps one chunk and runs the two 64-row blocks
     lens = np.full(128, 8192, dtype=np.int32)
-    for path in (gqla.ABSORB, gqla.GQA):
+    for path, want in ((gqla.ABSORB, (1, 8192)), (gqla.GQA, (2, 4096))):
         w, n, c = gqla.plan_splits_lens(FLAG, path, lens, 8192)
-        assert (n, c) == (2, 4096)
+        assert (n, c) == want
 
 
 def test_plan_lens_edges(lib):
