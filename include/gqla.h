@@ -31,12 +31,14 @@
  *     device, with its address looked up once per device).
  *   - q_rope and the k_R columns of the cache hold keys/queries with the
  *     rotary embedding already applied.
- *   - Operand range (bf16 storage): the kernels multiply fp16 copies of the bf16
- *     inputs on the MFMA units.  Values whose magnitude lies in fp16's normal range
- *     [2^-14, 65504] are converted exactly; smaller magnitudes keep fp16's subnormal
- *     spacing 2^-24 (an absolute error of at most 2^-24 per element); magnitudes above
- *     65504 are outside the supported range (they saturate).  This applies to the
- *     latent rows, k_R, the queries, the expanded rows of the GQA path and W_UK / W_UV.
+ *   - Operand range (bf16 storage): some products run on fp16 copies of the bf16
+ *     inputs: the GQA and sparse decodes' queries and expanded rows (k_R included),
+ *     and the latent rows c_t in the absorb decode's weighted sum u.  Values whose
+ *     magnitude lies in fp16's normal range [2^-14, 65504] are converted exactly;
+ *     smaller magnitudes keep fp16's subnormal spacing 2^-24 (an absolute error of at
+ *     most 2^-24 per element); magnitudes above 65504 are outside the supported range
+ *     (they saturate).  The absorb decode's scores, W_UK and W_UV, and the group
+ *     expansion use the bf16 values as given.
  *   - stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *     work on it and never synchronise; results are ready when the stream is.
  *   - Arguments are validated on the host before any launch; a failed check
@@ -132,8 +134,9 @@ gqla_status gqla_expand_groups(const gqla_shape* shape, int32_t batch, int32_t m
 /* MQA-absorb decode (section 2, memory-friendly path: the MLA form with group-indexed
  * up-projections): q~ = W_UK[j]^T q_nope per head, scores
  * s_t = scale [q~ | q_rope].[c_t | k_R,t], u = softmax-weighted sum of c_t,
- * o = W_UV[j] u.  The absorbed query is carried to about 22 significant bits, so the
- * result keeps the bf16 tolerance however peaked the softmax is.
+ * o = W_UV[j] u.  The absorbed query is carried as a bf16 pair (about 16 significant
+ * bits) against the latent rows as stored, so the result keeps the bf16 tolerance
+ * however peaked the softmax is.
  *   q_nope [batch][s_q][h_q][d_h], q_rope [batch][s_q][h_q][d_r]
  *   w_uk, w_uv [g][d_h][r_kv]; latent as in gqla_expand_groups
  *   out [batch][s_q][h_q][d_h] (dtype); lse (nullable) fp32 [batch][s_q][h_q],

@@ -25,17 +25,17 @@ constexpr int TT = 32;    // tokens per tile
 
 // Absorbed-query record of one query row, written by the prologue and read once by the
 // attention kernel (QREC bytes, 16-byte aligned):
-//   [0, 1024)     hi: fp16 of x' = q~ * scale * log2(e) * 2^E, latent column order
-//   [1024, 2048)  lo: fp16 of x' - hi (the rounding residual of hi, rounded again)
-//   [2048, 2176)  q^R as fp16 (exact for bf16 inputs in fp16's range), unscaled
-//   [2176, 2180)  2^-E (fp32); 2^E is a per-row power of two that puts max |x'| in
-//                 [2^13, 2^14), so hi stays finite and lo stays in fp16's normal range
-// hi + lo carries q~ to about 22 significant bits.  A single fp16 rounding of q~
-// (11 bits) gives score errors that grow with |score|: with sharp softmaxes (peak
-// logits of 30-40 in log2 units) they alone exceed the 2e-3 + 2e-2 |o| bound
-// several-fold, which the hi + lo pair removes at one extra MFMA per latent k-step.
-constexpr int QREC = 2192;
-constexpr int QHI = 0, QLO = 1024, QROPE = 2048, QINV = 2176;
+//   [0, 1024)     hi: bf16 of x = q~ * scale * log2(e), latent column order
+//   [1024, 2048)  lo: bf16 of x - hi (the rounding residual of hi, rounded again)
+//   [2048, 2176)  q^R (bf16, as given), unscaled
+// hi + lo carries x to about 16 significant bits, against the bf16 latent rows as they
+// are stored (every product exact in the fp32 accumulation).  A single 8- or 11-bit
+// rounding of q~ gives score errors that grow with |score|: with sharp softmaxes (peak
+// logits of 30-40 in log2 units) they alone exceed the 2e-3 + 2e-2 |o| bound several-
+// fold; the hi + lo pair leaves them far below it, at one extra MFMA per latent k-step.
+// bf16 keeps fp32's exponent range, so no operand of the score product needs scaling.
+constexpr int QREC = 2176;
+constexpr int QHI = 0, QLO = 1024, QROPE = 2048;
 
 // ---------------------------------------------------------------------------
 // Prologue: one block per (64 rows of group j, j); 4 waves of 16 rows.  Rows of group j
@@ -118,49 +118,29 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
         }
     }
 
-    // x = q~ * scale * log2(e); the row's largest |x| (over its four lanes) sets 2^E
-    float mx = 0.f;
-#pragma unroll
-    for (int c = 0; c < RK / 16; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[c][i] *= scale_log2;
-            mx = fmaxf(mx, fabsf(acc[c][i]));
-        }
-    mx = wave_max16x4(mx);
-    int ex = 0;
-    (void)frexpf(mx, &ex);                        // mx = f 2^ex, f in [0.5, 1); ex = 0 for mx = 0
-    const int E = mx > 0.f ? 14 - ex : 0;         // max |x'| in [2^13, 2^14)
-    const float up = ldexpf(1.f, E), inv = ldexpf(1.f, -E);
     if (!ok) return;
+    // x = q~ * scale * log2(e) (fp32) as hi = bf16(x) and lo = bf16(x - hi)
 #pragma unroll
     for (int c = 0; c < RK / 16; ++c) {
         // columns 16 c + 4 q4 + i of the natural latent order (c = 8 qc + mt)
         const int col = 16 * c + 4 * q4;
-        float xs[4], rs[4];
+        u16 hs[4], ls[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            xs[i] = acc[c][i] * up;
-            const float hv = (float)(_Float16)xs[i];
-            rs[i] = xs[i] - hv;
-            xs[i] = hv;
+            const float x = acc[c][i] * scale_log2;
+            hs[i] = f2bf(x);
+            ls[i] = f2bf(x - bf2f(hs[i]));
         }
-        u32x2 vh, vl;
-        vh[0] = pack2h(xs[0], xs[1]);
-        vh[1] = pack2h(xs[2], xs[3]);
-        vl[0] = pack2h(rs[0], rs[1]);
-        vl[1] = pack2h(rs[2], rs[3]);
-        *reinterpret_cast<u32x2*>(dst + QHI + col * 2) = vh;
-        *reinterpret_cast<u32x2*>(dst + QLO + col * 2) = vl;
+        *reinterpret_cast<u32x2*>(dst + QHI + col * 2) = u32x2{pack2(hs[0], hs[1]), pack2(hs[2], hs[3])};
+        *reinterpret_cast<u32x2*>(dst + QLO + col * 2) = u32x2{pack2(ls[0], ls[1]), pack2(ls[2], ls[3])};
     }
-    // q^R: 64 elements; lane group q4 converts elements 16 q4 .. 16 q4 + 15 to fp16
+    // q^R: 64 elements; lane group q4 copies elements 16 q4 .. 16 q4 + 15
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int off = q4 * 16 + c * 8;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(q_rope + qrow * DR + off);
-        *reinterpret_cast<u32x4*>(dst + QROPE + off * 2) = bf8_to_h8(v);
+        *reinterpret_cast<u32x4*>(dst + QROPE + off * 2) =
+            *reinterpret_cast<const u32x4*>(q_rope + qrow * DR + off);
     }
-    if (q4 == 0) *reinterpret_cast<float*>(dst + QINV) = inv;
 }
 
 // ---------------------------------------------------------------------------
@@ -172,48 +152,50 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
 //     whole tile's 32 tokens.  It holds that row tile's absorbed queries in registers
 //     (hi, lo and rotary parts: 136 VGPRs), computes
 //       S^T[token][row] = C_tile . q^T   (A = latent rows from LDS, B = queries)
-//     on the 16x16x32 fp16 MFMA, keeps the online softmax state of its rows and writes
+//     on the 16x16x32 bf16 MFMA, keeps the online softmax state of its rows and writes
 //     P (fp16, in the B-operand layout of the value MFMA) and each row's rescale
 //     factor to LDS.
 //   - 4 value waves: value wave v owns latent columns 128 v .. 128 v + 127 of u for all
 //     R rows (u: 128 VGPRs at R = 64) and computes
 //       U^T[col][row] += C_tile^T . P^T  (A = latent columns from LDS with the gfx950
-//                                          transposing read, B = P from LDS).
-//     Value waves also stream the tiles from HBM and convert them.
+//                                          transposing read, B = P from LDS)
+//     on the 16x16x32 fp16 MFMA, converting its A operands from bf16 in registers.
+//     Value waves also stream the tiles from HBM.
 // Waves w and w + 4 share a SIMD, so at R = 64 each SIMD runs one score and one value
-// wave: the score wave's softmax (VALU) runs beside the value wave's MFMAs and the value
-// wave's tile conversion beside the score wave's MFMAs.  Splitting u by columns over
-// value waves and q by rows over score waves keeps both within 256 registers: u for 128
-// rows is 256 KB and q^ (hi + lo) 278 KB, more than a CU's 512 KB register file
-// together, so a workgroup takes 64 rows and the 2 (s_q = 1) or 4 (s_q = 2) row blocks
-// of a (chunk, sequence) pair run as workgroups 8 ids apart, on one XCD, where the
-// second read of every tile is an L2 hit.
+// wave: the score wave's softmax (VALU) runs beside the value wave's MFMAs.  Splitting u
+// by columns over value waves and q by rows over score waves keeps both within 256
+// registers: u for 128 rows is 256 KB and q^ (hi + lo) 278 KB, more than a CU's 512 KB
+// register file together, so a workgroup takes 64 rows and the 2 (s_q = 1) or 4
+// (s_q = 2) row blocks of a (chunk, sequence) pair run as workgroups 8 ids apart, on one
+// XCD, where the second read of every tile is an L2 hit.
 //
-// Pipeline.  Tiles (32 rows x 576, one contiguous span of HBM) go straight from global
-// memory into LDS with global_load_lds_dwordx4 (lane l of a wave instruction lands at
-// base + 16 l), into four buffers.  At step k, after the barrier that published tile k:
+// Pipeline.  Tiles (32 rows x 576 bf16, one contiguous span of HBM) go straight from
+// global memory into LDS with global_load_lds_dwordx4 (lane l of a wave instruction
+// lands at base + 16 l), into four buffers, and are used there as loaded: nothing is
+// written to a tile buffer but the loads themselves (LDS writes run at well under half
+// the read rate on gfx950, so a conversion pass through LDS would cost as much as all
+// the operand reads).  At step k, after the barrier that published tile k:
 //   score waves:  scores and softmax of tile k (buffer k%4), P and rescale factors to
 //                 the P buffer k%2;
-//   value waves:  issue the loads of tile k+2 (buffer (k+2)%4, last read at step k-1),
-//                 then U += C_{k-1}^T P_{k-1} (buffer (k-1)%4, P buffer (k-1)%2) with the
-//                 in-place bf16 -> fp16 conversion of tile k+1 (buffer (k+1)%4, loaded
-//                 at step k-1) spread over those MFMAs; each value wave converts the
-//                 slots it loaded itself, so it only waits on its own loads;
-// then one barrier.  LDS: 4 tiles of 32 x (576 + 16) fp16 (148 KB) + 2 P buffers.  Rows
+//   value waves:  U += C_{k-1}^T P_{k-1} (buffer (k-1)%4, P buffer (k-1)%2), with the
+//                 loads of tile k+2 (buffer (k+2)%4, last read at step k-1) issued
+//                 between those MFMAs; then each waits until its own loads of tile k+1
+//                 (issued at step k-1) have landed;
+// then one barrier.  LDS: 4 tiles of 32 x (576 + 16) bf16 (148 KB) + 2 P buffers.  Rows
 // past the chunk are loaded as copies of the tile's first row (finite data, P = 0).
 // The row stride of 576 + 16 elements (8 x odd dwords modulo the 64 banks) keeps both
 // the 16-byte operand reads of 16 rows and the transposing reads of 4 rows x 32 bytes
-// free of bank conflicts.
+// free of bank conflicts (measured at the full LDS read rate on gfx950).
 //
-// Scores.  x' = hi + lo (per-row scale 2^E) against the tile's fp16 latent (exact for
-// bf16 data within fp16's range) accumulates 2^E times the latent part of the log2-domain
-// logit; the rotary part multiplies exact fp16 copies of q^R and k_R and is scaled after
-// the MFMA: s = acc * 2^-E + scale log2(e) accr.
+// Scores.  x = hi + lo against the tile's bf16 latent accumulates the latent part of the
+// log2-domain logit; the rotary part multiplies q^R and k_R as given and is scaled after
+// the MFMA: s = acc + scale log2(e) accr.
 //
 // Softmax.  Online, with a lazily raised reference: exponentials are taken against a
 // per-row reference m (log2 domain) raised only when a tile's maximum exceeds it by more
 // than kLazy, so p = 2^(s - m) <= 2^kLazy, which fp16 P and fp32 sums hold as precisely as
-// values <= 1.  When a row that has accumulated raises its reference, the value waves
+// values <= 1.  P is fp16 rather than bf16: its 11-bit significand keeps the weights'
+// rounding well inside the bound, where bf16's 8 bits would exceed it on sharp softmaxes.  When a row that has accumulated raises its reference, the value waves
 // multiply its u columns by alpha = 2^(m_old - m_new) before adding the tile; the score
 // wave writes alpha (1 otherwise) beside P.  Normalisation and log-sum-exp use the same
 // reference, so the result is the exact softmax's.
@@ -371,8 +353,7 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
         // ============================== score wave: row tile sw
         const int sw = wave;
         const bool active = sw < na;
-        f16x8 qhi[RK / 32], qlo[RK / 32], qro[DR / 32];
-        float qinv = 0.f;
+        bf16x8 qhi[RK / 32], qlo[RK / 32], qro[DR / 32];
         int nvis = 0;
         SoftmaxState st{kNegInf, 0.f};
         if (active) {
@@ -380,13 +361,12 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
             const unsigned char* rec = qrec + ((size_t)b * RQ + rho) * QREC;
 #pragma unroll
             for (int kk = 0; kk < RK / 32; ++kk) {
-                qhi[kk] = ld_f16x8(reinterpret_cast<const u16*>(rec + QHI) + kk * 32 + q4 * 8);
-                qlo[kk] = ld_f16x8(reinterpret_cast<const u16*>(rec + QLO) + kk * 32 + q4 * 8);
+                qhi[kk] = ld_bf16x8(reinterpret_cast<const u16*>(rec + QHI) + kk * 32 + q4 * 8);
+                qlo[kk] = ld_bf16x8(reinterpret_cast<const u16*>(rec + QLO) + kk * 32 + q4 * 8);
             }
 #pragma unroll
             for (int kr = 0; kr < DR / 32; ++kr)
-                qro[kr] = ld_f16x8(reinterpret_cast<const u16*>(rec + QROPE) + kr * 32 + q4 * 8);
-            qinv = *reinterpret_cast<const float*>(rec + QINV);
+                qro[kr] = ld_bf16x8(reinterpret_cast<const u16*>(rec + QROPE) + kr * 32 + q4 * 8);
             nvis = clampi(L - s_q + rho / h_q + 1, 0, L);
         }
         auto sstep = [&](int k) {
@@ -401,35 +381,35 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
                 // after); its operand reads are issued PF steps ahead of its MFMAs, which the
                 // scheduling barriers keep in this order
                 constexpr int KS = W / 32, PF = 3;
-                f16x8 ra0[PF + 1], ra1[PF + 1];
+                bf16x8 ra0[PF + 1], ra1[PF + 1];
 #pragma unroll
                 for (int j = 0; j < PF; ++j) {
-                    ra0[j] = ld_f16x8(arow + j * 32);
-                    ra1[j] = ld_f16x8(arow + 16 * STRIDE + j * 32);
+                    ra0[j] = ld_bf16x8(arow + j * 32);
+                    ra1[j] = ld_bf16x8(arow + 16 * STRIDE + j * 32);
                 }
 #pragma unroll
                 for (int j = 0; j < KS; ++j) {
                     if (j + PF < KS) {
-                        ra0[(j + PF) % (PF + 1)] = ld_f16x8(arow + (j + PF) * 32);
-                        ra1[(j + PF) % (PF + 1)] = ld_f16x8(arow + 16 * STRIDE + (j + PF) * 32);
+                        ra0[(j + PF) % (PF + 1)] = ld_bf16x8(arow + (j + PF) * 32);
+                        ra1[(j + PF) % (PF + 1)] = ld_bf16x8(arow + 16 * STRIDE + (j + PF) * 32);
                     }
-                    const f16x8 a0 = ra0[j % (PF + 1)], a1 = ra1[j % (PF + 1)];
+                    const bf16x8 a0 = ra0[j % (PF + 1)], a1 = ra1[j % (PF + 1)];
                     if (j < RK / 32) {
-                        acc0 = mfma16h(a0, qhi[j], acc0);
-                        acc1 = mfma16h(a1, qhi[j], acc1);
-                        acc0 = mfma16h(a0, qlo[j], acc0);
-                        acc1 = mfma16h(a1, qlo[j], acc1);
+                        acc0 = mfma16(a0, qhi[j], acc0);
+                        acc1 = mfma16(a1, qhi[j], acc1);
+                        acc0 = mfma16(a0, qlo[j], acc0);
+                        acc1 = mfma16(a1, qlo[j], acc1);
                     } else {
-                        accr0 = mfma16h(a0, qro[j - RK / 32], accr0);
-                        accr1 = mfma16h(a1, qro[j - RK / 32], accr1);
+                        accr0 = mfma16(a0, qro[j - RK / 32], accr0);
+                        accr1 = mfma16(a1, qro[j - RK / 32], accr1);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 float sc[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    sc[i] = fmaf(accr0[i], scale_log2, acc0[i] * qinv);
-                    sc[4 + i] = fmaf(accr1[i], scale_log2, acc1[i] * qinv);
+                    sc[i] = fmaf(accr0[i], scale_log2, acc0[i]);
+                    sc[4 + i] = fmaf(accr1[i], scale_log2, acc1[i]);
                 }
                 if (tb + TT > t_full) {
 #pragma unroll
@@ -495,7 +475,7 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
         // two 16-bit offsets per register (a tile is 36,864 bytes).  The 37 instructions of a
         // tile cover its 2368 slots exactly; the two pad slots of an LDS row load that row's
         // first 16 bytes (a line the row's first slot loads anyway) and are never read, so
-        // every slot loads and converts without a condition.
+        // every instruction loads all 64 lanes without a condition.
         static_assert(NINST * 64 == TSLOTS, "load instructions cover the tile exactly");
         uint32_t dma_off2[(VI + 1) / 2];
 #pragma unroll
@@ -515,25 +495,24 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
 #pragma unroll
             for (int i = 0; i < (VI + 1) / 2; ++i) asm volatile("" : "+v"(dma_off2[i]));
         };
-        const int vslot = vw * 64 + lane;   // slot of instruction 0; instruction i adds 4 * 64 i
         const bool full = vw < NINST % NV || NINST % NV == 0;   // this wave issues VI loads per tile (else VI - 1)
-        // Direct loads of tile `it` into the buffer at LDS byte address tbuf: instruction i of
-        // value wave vw fills slots (vw + 4 i) * 64 .. + 63.  Rows past the chunk load the
-        // tile's first row instead.
+        // Instruction i of value wave vw fills slots (vw + 4 i) * 64 .. + 63 of a tile buffer.
+        auto dma_one = [&](const u16* tsrc, uint32_t off, uint32_t tbuf, int i) {
+            if (i < VI - 1 || full) dma16(tsrc, off, tbuf + (uint32_t)((vw + NV * i) * 1024));
+        };
+        // All loads of tile `it` at once; rows past the chunk load the tile's first row.
         auto dma_tile = [&](int it, uint32_t tbuf) {
             const u16* tsrc = seq + (size_t)it * TT * W;
             const int rows = t1 - t0 - it * TT;
             if (rows >= TT) {
 #pragma unroll
-                for (int i = 0; i < VI; ++i)
-                    if (i < VI - 1 || full) dma16(tsrc, slot_off(i), tbuf + (uint32_t)((vw + NV * i) * 1024));
+                for (int i = 0; i < VI; ++i) dma_one(tsrc, slot_off(i), tbuf, i);
             } else {
                 const uint32_t lim = (uint32_t)(rows * W * 2);
 #pragma unroll
                 for (int i = 0; i < VI; ++i) {
                     const uint32_t o = slot_off(i);
-                    if (i < VI - 1 || full)
-                        dma16(tsrc, o < lim ? o : o % (uint32_t)(W * 2), tbuf + (uint32_t)((vw + NV * i) * 1024));
+                    dma_one(tsrc, o < lim ? o : o % (uint32_t)(W * 2), tbuf, i);
                 }
             }
         };
@@ -548,51 +527,38 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
                 wait_vmcnt<VI - 1>();
             }
         };
-        // tb: the tile buffer already offset to this lane's first slot (tb + vslot * 8)
-        auto convert_slot = [&](u16* tb, int i) {
-            if (i < VI - 1 || full) {
-                u16* ptr = tb + i * NV * 64 * 8;
-                *reinterpret_cast<u32x4*>(ptr) = bf8_to_h8(*reinterpret_cast<const u32x4*>(ptr));
-            }
-        };
         // lane offset of the transposing reads of column tile 0 of this wave's columns
         const int goff = (4 * q4 + (r16 >> 2)) * STRIDE + VCOLS * vw + 4 * (r16 & 3);
-        // Step k >= 1 of the pipeline.  The conversion of tile k+1 runs unconditionally: when
-        // there is no tile k+1 its buffer (that of tile k-3) is free and holds data nobody
-        // reads, so the value MFMAs run as one straight sequence.
+        // Step k >= 1 of the pipeline: U += C_{k-1}^T P_{k-1}, loads of tile k+2, wait for
+        // this wave's loads of tile k+1.
         auto vstep = [&](int k) {
             opaque_offsets();
             // per-lane bases, opaque per step: the addresses derived from them are then
             // recomputed in each step (one add each) instead of being hoisted out of the
             // loop for all four buffers and held in registers
-            int vs = vslot, go = goff, ln = lane;
-            asm volatile("" : "+v"(vs), "+v"(go), "+v"(ln));
-            u16* const cbase = bufp(k + 1) + vs * 8;   // tile k+1 (converted this step)
+            int go = goff, ln = lane;
+            asm volatile("" : "+v"(go), "+v"(ln));
             const u16* const bval = bufp(k + 3);       // tile k-1
             const u16* const pr = pbuf[(k + 1) & 1];
             const float* const ar = abuf[(k + 1) & 1];
             const bool more = k + 2 < ntiles;
-            if (more) dma_tile(k + 2, lds_addr(bufp(k + 2)));
-            // rescale rows whose reference rose at tile k-1 (rare)
+            // a full next tile's loads are spread over the MFMAs below; a partial one (the
+            // chunk's last) is issued here at once
+            const bool spread = more && t1 - t0 - (k + 2) * TT >= TT;
+            if (more && !spread) dma_tile(k + 2, lds_addr(bufp(k + 2)));
+            const u16* const nsrc = seq + (size_t)(k + 2) * TT * W;
+            const uint32_t nbuf = lds_addr(bufp(k + 2));
+            // all reads that start the step are issued before the first wait: the rescale
+            // factors, P, and the first A operands (transposing reads of 16-column tiles of
+            // bf16, kept PV column tiles ahead of their MFMAs and converted to fp16 just
+            // before them)
             float al[NS];
 #pragma unroll
             for (int rt = 0; rt < NS; ++rt) al[rt] = ar[16 * rt + (ln & 15)];
-            bool any = false;
-#pragma unroll
-            for (int rt = 0; rt < NS; ++rt) any = any || al[rt] != 1.f;
-            if (__builtin_expect(__any(any), 0)) {
-                asm volatile("" ::: "memory");
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int rt = 0; rt < NS; ++rt) uacc[ct][rt] *= al[rt];
-            }
             f16x8 pv[NS];
 #pragma unroll
             for (int rt = 0; rt < NS; ++rt) pv[rt] = ld_f16x8(pr + (rt * 64 + ln) * 8);
-            // A operands (transposing reads of a 16-column tile) are read two column tiles
-            // ahead of their MFMAs
-            constexpr int PV = 2;
+            constexpr int PV = 3;
             u32x4 ra[PV + 1];
             auto read_a = [&](int ct) -> u32x4 {
                 const u16* p0 = bval + go + 16 * ct;
@@ -602,42 +568,44 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
             };
 #pragma unroll
             for (int c = 0; c < PV; ++c) ra[c] = read_a(c);
-            // this wave's slots of tile k+1: all read once their loads have landed, then
-            // converted and written back one or two per column tile
-            wait_own(more);
-            u32x4 cv[VI];
+            // rescale rows whose reference rose at tile k-1 (rare)
+            bool any = false;
 #pragma unroll
-            for (int i = 0; i < VI; ++i)
-                if (i < VI - 1 || full) cv[i] = *reinterpret_cast<const u32x4*>(cbase + i * NV * 64 * 8);
+            for (int rt = 0; rt < NS; ++rt) any = any || al[rt] != 1.f;
+            if (__builtin_expect(__any(any), 0)) {
+                asm volatile("" ::: "memory");   // keeps the multiplies inside the branch
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int rt = 0; rt < NS; ++rt) uacc[ct][rt] *= al[rt];
+            }
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 if (ct + PV < NCT) ra[(ct + PV) % (PV + 1)] = read_a(ct + PV);
-                const f16x8 a = as_f16x8(ra[ct % (PV + 1)]);
+                const f16x8 a = as_f16x8(bf8_to_h8(ra[ct % (PV + 1)]));
 #pragma unroll
                 for (int rt = 0; rt < NS; ++rt) uacc[ct][rt] = mfma16h(a, pv[rt], uacc[ct][rt]);
+                if (spread) {
 #pragma unroll
-                for (int i = 0; i < VI; ++i)
-                    if (i * NCT / VI == ct && (i < VI - 1 || full))
-                        *reinterpret_cast<u32x4*>(cbase + i * NV * 64 * 8) = bf8_to_h8(cv[i]);
+                    for (int i = 0; i < VI; ++i)
+                        if (i * NCT / VI == ct) dma_one(nsrc, slot_off(i), nbuf, i);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            wait_own(more);
             block_sync();
         };
-        // prologue of the pipeline: tiles 0 and 1 loaded, tile 0 converted; then step 0
-        // (loads of tile 2, conversion of tile 1)
+        // prologue of the pipeline: tiles 0 and 1 issued, tile 0 landed; then step 0 (loads
+        // of tile 2, tile 1 landed)
         dma_tile(0, lds_addr(bufp(0)));
         const bool two = ntiles > 1;
         if (two) dma_tile(1, lds_addr(bufp(1)));
         wait_own(two);
-#pragma unroll
-        for (int i = 0; i < VI; ++i) convert_slot(bufp(0) + vslot * 8, i);
         block_sync();
         {
             const bool more = 2 < ntiles;
             if (more) dma_tile(2, lds_addr(bufp(2)));
             wait_own(more);
-#pragma unroll
-            for (int i = 0; i < VI; ++i) convert_slot(bufp(1) + vslot * 8, i);
             block_sync();
         }
 #pragma unroll 1
@@ -662,17 +630,22 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
             float* blk = red + rt * 8 * 64 * 4;
             const float l = lfin[16 * rt + r16];
             const float inv = l > 0.f ? 1.f / l : 0.f;
-            // U^T as the B operand of o^T = W_UV[j] U^T: k-step ks covers latent columns
-            // VCOLS vw + 32 ks + (token slot order of P), which are column tiles 2ks and
-            // 2ks + 1 of u, element e%4.  u / l is carried as three bf16 terms (about 24
+            // U^T as the B operand of o^T = W_UV[j] U^T: in k-step ks, k-slot e of lane group
+            // q4 is latent column VCOLS vw + 32 ks + 8 q4 + e, so that each lane's weight
+            // operand is 16 contiguous bytes of a W_UV row.  Column 16 ct + 4 q + i of u sits
+            // in column tile ct, lane r16 + 16 q, element i of the stored accumulators, so
+            // slots 0-3 come from lane group 2 (q4 & 1) and slots 4-7 from the next one, of
+            // column tile 2 ks + q4 / 2.  u / l is carried as three bf16 terms (about 24
             // significant bits): o = W_UV u can cancel to values far below |u| (a one-hot
             // softmax over latent rows of magnitude 1e4 leaves u = c_t), and two terms
             // (16 bits) would then miss the 2e-3 absolute bound.
             bf16x8 ub[NCT / 2], um[NCT / 2], ul[NCT / 2];
+            const int lq = r16 + 32 * (q4 & 1);
 #pragma unroll
             for (int ks = 0; ks < NCT / 2; ++ks) {
-                const floatx4 c0 = *reinterpret_cast<const floatx4*>(blk + ((2 * ks) * 64 + lane) * 4);
-                const floatx4 c1 = *reinterpret_cast<const floatx4*>(blk + ((2 * ks + 1) * 64 + lane) * 4);
+                const int ctq = 2 * ks + (q4 >> 1);
+                const floatx4 c0 = *reinterpret_cast<const floatx4*>(blk + (ctq * 64 + lq) * 4);
+                const floatx4 c1 = *reinterpret_cast<const floatx4*>(blk + (ctq * 64 + lq + 16) * 4);
                 u32x4 vh, vm, vl;
 #pragma unroll
                 for (int hh = 0; hh < 4; ++hh) {
@@ -698,17 +671,13 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
             for (int jj = jlo; jj <= jhi; ++jj) {
                 // all of the group's weight operands for this wave's columns are loaded
                 // before the first MFMA (one round trip to L2 per row tile and group)
-                const u16* wrow = w_uv + (size_t)jj * DH * RK + VCOLS * vw + (size_t)r16 * RK + q4 * 4;
+                const u16* wrow = w_uv + (size_t)jj * DH * RK + VCOLS * vw + (size_t)r16 * RK + q4 * 8;
                 u32x4 wa[DH / 16][NCT / 2];
 #pragma unroll
                 for (int dt = 0; dt < DH / 16; ++dt)
 #pragma unroll
-                    for (int ks = 0; ks < NCT / 2; ++ks) {
-                        const u16* pw = wrow + (size_t)dt * 16 * RK + ks * 32;
-                        const u32x2 lo = *reinterpret_cast<const u32x2*>(pw);
-                        const u32x2 hi = *reinterpret_cast<const u32x2*>(pw + 16);
-                        wa[dt][ks] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                    }
+                    for (int ks = 0; ks < NCT / 2; ++ks)
+                        wa[dt][ks] = *reinterpret_cast<const u32x4*>(wrow + (size_t)dt * 16 * RK + ks * 32);
 #pragma unroll
                 for (int dt = 0; dt < DH / 16; ++dt) {
                     floatx4 acc = {0.f, 0.f, 0.f, 0.f};

@@ -152,9 +152,9 @@ def test_sharp_sparse(gqla, s_q):
                ref=lambda b, L: oracle.sparse_gqa_decode(stored[b], qn[b], qr[b], cfg.g, idx[b], L, cfg.scale))
 
 
-# Operand range.  The kernels feed the MFMA fp16 operands converted from bf16 storage:
-# exact for magnitudes in fp16's normal range [2^-14, 65504]; smaller values keep fp16's
-# subnormal spacing 2^-24.
+# Operand range.  Some products run on fp16 copies of the bf16 inputs (the GQA path's
+# queries and expanded rows, the absorb path's latent rows in u): exact for magnitudes in
+# fp16's normal range [2^-14, 65504]; smaller values keep fp16's subnormal spacing 2^-24.
 #   Small values: latent rows of RMS 1e-4 and 1e-5 (mostly below 2^-14) meet the bound
 #   as it is written (their outputs are small; the absolute term covers the subnormal
 #   rounding).
