@@ -162,7 +162,9 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
 //     on the 16x16x32 fp16 MFMA, converting its A operands from bf16 in registers.
 //     Value waves also stream the tiles from HBM.
 // Waves w and w + 4 share a SIMD, so at R = 64 each SIMD runs one score and one value
-// wave: the score wave's softmax (VALU) runs beside the value wave's MFMAs.  Splitting u
+// wave.  Score waves issue at a raised priority: their MFMAs go first, and the value
+// wave's operand conversion (VALU) runs beside them; the value wave's MFMAs follow,
+// beside the score wave's softmax.  Splitting u
 // by columns over value waves and q by rows over score waves keeps both within 256
 // registers: u for 128 rows is 256 KB and q^ (hi + lo) 278 KB, more than a CU's 512 KB
 // register file together, so a workgroup takes 64 rows and the 2 (s_q = 1) or 4
@@ -177,10 +179,9 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
 // the operand reads).  At step k, after the barrier that published tile k:
 //   score waves:  scores and softmax of tile k (buffer k%4), P and rescale factors to
 //                 the P buffer k%2;
-//   value waves:  U += C_{k-1}^T P_{k-1} (buffer (k-1)%4, P buffer (k-1)%2), with the
-//                 loads of tile k+2 (buffer (k+2)%4, last read at step k-1) issued
-//                 between those MFMAs; then each waits until its own loads of tile k+1
-//                 (issued at step k-1) have landed;
+//   value waves:  issue the loads of tile k+2 (buffer (k+2)%4, last read at step k-1),
+//                 then U += C_{k-1}^T P_{k-1} (buffer (k-1)%4, P buffer (k-1)%2), then
+//                 wait until their own loads of tile k+1 (issued at step k-1) have landed;
 // then one barrier.  LDS: 4 tiles of 32 x (576 + 16) bf16 (148 KB) + 2 P buffers.  Rows
 // past the chunk are loaded as copies of the tile's first row (finite data, P = 0).
 // The row stride of 576 + 16 elements (8 x odd dwords modulo the 64 banks) keeps both
@@ -351,6 +352,9 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
     // never holds the score waves' queries and the value waves' accumulators at once.
     if (wave < NS) {
         // ============================== score wave: row tile sw
+        // Its MFMAs go first on the SIMD; the value wave's MFMAs fill in behind them,
+        // mostly while this wave runs its softmax.
+        __builtin_amdgcn_s_setprio(1);
         const int sw = wave;
         const bool active = sw < na;
         bf16x8 qhi[RK / 32], qlo[RK / 32], qro[DR / 32];
@@ -380,7 +384,7 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
                 // k-step j = 0..17 reads columns 32 j .. 32 j + 31 (latent for j < 16, rotary
                 // after); its operand reads are issued PF steps ahead of its MFMAs, which the
                 // scheduling barriers keep in this order
-                constexpr int KS = W / 32, PF = 3;
+                constexpr int KS = W / 32, PF = 6;
                 bf16x8 ra0[PF + 1], ra1[PF + 1];
 #pragma unroll
                 for (int j = 0; j < PF; ++j) {
@@ -451,7 +455,6 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
         block_sync();   // tile 0 converted
 #pragma unroll 1
         for (int k = 0; k <= ntiles; ++k) sstep(k);
-        block_sync();   // value waves' epilogue partials written
         if (active && q4 == 0) {
             const int rho = z * R + 16 * sw + r16;
             const int s = rho / h_q, h = rho - (rho / h_q) * h_q;
@@ -542,32 +545,27 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
             const u16* const pr = pbuf[(k + 1) & 1];
             const float* const ar = abuf[(k + 1) & 1];
             const bool more = k + 2 < ntiles;
-            // a full next tile's loads are spread over the MFMAs below; a partial one (the
-            // chunk's last) is issued here at once
-            const bool spread = more && t1 - t0 - (k + 2) * TT >= TT;
-            if (more && !spread) dma_tile(k + 2, lds_addr(bufp(k + 2)));
-            const u16* const nsrc = seq + (size_t)(k + 2) * TT * W;
-            const uint32_t nbuf = lds_addr(bufp(k + 2));
-            // all reads that start the step are issued before the first wait: the rescale
-            // factors, P, and the first A operands (transposing reads of 16-column tiles of
-            // bf16, kept PV column tiles ahead of their MFMAs and converted to fp16 just
-            // before them)
+            // the loads of tile k+2 go out first: they have until the end of step k+1 to land
+            if (more) dma_tile(k + 2, lds_addr(bufp(k + 2)));
+            // All of the step's LDS reads are issued before the first wait: the rescale
+            // factors, P, and the A operands of all eight column tiles (transposing reads
+            // of bf16).  The A operands are then converted to fp16, and only after that do
+            // the MFMAs start: the conversion (VALU) runs beside the score wave's MFMAs on
+            // this SIMD, and this wave's MFMAs beside the score wave's softmax.
             float al[NS];
 #pragma unroll
             for (int rt = 0; rt < NS; ++rt) al[rt] = ar[16 * rt + (ln & 15)];
             f16x8 pv[NS];
 #pragma unroll
             for (int rt = 0; rt < NS; ++rt) pv[rt] = ld_f16x8(pr + (rt * 64 + ln) * 8);
-            constexpr int PV = 3;
-            u32x4 ra[PV + 1];
-            auto read_a = [&](int ct) -> u32x4 {
+            u32x4 ra[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
                 const u16* p0 = bval + go + 16 * ct;
                 const u32x2 lo = lds_read_tr16(p0);
                 const u32x2 hi = lds_read_tr16(p0 + 16 * STRIDE);
-                return u32x4{lo[0], lo[1], hi[0], hi[1]};
-            };
-#pragma unroll
-            for (int c = 0; c < PV; ++c) ra[c] = read_a(c);
+                ra[ct] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
             // rescale rows whose reference rose at tile k-1 (rare)
             bool any = false;
 #pragma unroll
@@ -580,16 +578,13 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
                     for (int rt = 0; rt < NS; ++rt) uacc[ct][rt] *= al[rt];
             }
 #pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) ra[ct] = bf8_to_h8(ra[ct]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                if (ct + PV < NCT) ra[(ct + PV) % (PV + 1)] = read_a(ct + PV);
-                const f16x8 a = as_f16x8(bf8_to_h8(ra[ct % (PV + 1)]));
+                const f16x8 a = as_f16x8(ra[ct]);
 #pragma unroll
                 for (int rt = 0; rt < NS; ++rt) uacc[ct][rt] = mfma16h(a, pv[rt], uacc[ct][rt]);
-                if (spread) {
-#pragma unroll
-                    for (int i = 0; i < VI; ++i)
-                        if (i * NCT / VI == ct) dma_one(nsrc, slot_off(i), nbuf, i);
-                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             wait_own(more);
@@ -613,86 +608,91 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
         // no direct load may still be writing this workgroup's LDS
         wait_vmcnt<0>();
 
-        // ---- epilogue: o^T = W_UV[j] (u / l)^T, a partial sum over this wave's columns.
-        // u goes to tile buffer vw first (free: the last step's barrier retired every tile),
-        // as 8 KB per row tile; each row tile is then read back, multiplied, and its partial
-        // (also 8 KB) written over it.  Storing u at once ends the accumulators' lives at
-        // the loop exit, so the epilogue never holds them next to its own registers.
+        // u goes to tile buffer vw (free: the last step's barrier retired every tile), as
+        // 8 KB per row tile.  Storing it at once ends the accumulators' lives at the loop
+        // exit, so the epilogue never holds them next to its own registers.
         float* red = reinterpret_cast<float*>(bufp(vw));
 #pragma unroll
         for (int rt = 0; rt < NS; ++rt)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
                 *reinterpret_cast<floatx4*>(red + (((rt * 8) + ct) * 64 + lane) * 4) = uacc[ct][rt];
-        const int hpg = h_q / g;
+    }
+    block_sync();   // u of every column block is in LDS
+
+    // ---- epilogue: o^T = W_UV[j] (u / l)^T.  Unit (row tile rt, column block cb) is the
+    // partial sum over latent columns VCOLS cb .. + VCOLS - 1 for the 16 rows of rt; the
+    // units are dealt over all waves (score waves included), and each writes its partial
+    // (8 KB) over the u it read.
+    const int hpg = h_q / g;
 #pragma unroll 1
-        for (int rt = 0; rt < na; ++rt) {
-            float* blk = red + rt * 8 * 64 * 4;
-            const float l = lfin[16 * rt + r16];
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            // U^T as the B operand of o^T = W_UV[j] U^T: in k-step ks, k-slot e of lane group
-            // q4 is latent column VCOLS vw + 32 ks + 8 q4 + e, so that each lane's weight
-            // operand is 16 contiguous bytes of a W_UV row.  Column 16 ct + 4 q + i of u sits
-            // in column tile ct, lane r16 + 16 q, element i of the stored accumulators, so
-            // slots 0-3 come from lane group 2 (q4 & 1) and slots 4-7 from the next one, of
-            // column tile 2 ks + q4 / 2.  u / l is carried as three bf16 terms (about 24
-            // significant bits): o = W_UV u can cancel to values far below |u| (a one-hot
-            // softmax over latent rows of magnitude 1e4 leaves u = c_t), and two terms
-            // (16 bits) would then miss the 2e-3 absolute bound.
-            bf16x8 ub[NCT / 2], um[NCT / 2], ul[NCT / 2];
-            const int lq = r16 + 32 * (q4 & 1);
+    for (int un = wave; un < na * NV; un += NS + NV) {
+        const int rt = un / NV, cb = un - (un / NV) * NV;
+        float* blk = reinterpret_cast<float*>(bufp(cb)) + rt * 8 * 64 * 4;
+        const float l = lfin[16 * rt + r16];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        // U^T as the B operand of o^T = W_UV[j] U^T: in k-step ks, k-slot e of lane group
+        // q4 is latent column VCOLS cb + 32 ks + 8 q4 + e, so that each lane's weight
+        // operand is 16 contiguous bytes of a W_UV row.  Column 16 ct + 4 q + i of u sits
+        // in column tile ct, lane r16 + 16 q, element i of the stored accumulators, so
+        // slots 0-3 come from lane group 2 (q4 & 1) and slots 4-7 from the next one, of
+        // column tile 2 ks + q4 / 2.  u / l is carried as three bf16 terms (about 24
+        // significant bits): o = W_UV u can cancel to values far below |u| (a one-hot
+        // softmax over latent rows of magnitude 1e4 leaves u = c_t), and two terms
+        // (16 bits) would then miss the 2e-3 absolute bound.
+        bf16x8 ub[NCT / 2], um[NCT / 2], ul[NCT / 2];
+        const int lq = r16 + 32 * (q4 & 1);
 #pragma unroll
-            for (int ks = 0; ks < NCT / 2; ++ks) {
-                const int ctq = 2 * ks + (q4 >> 1);
-                const floatx4 c0 = *reinterpret_cast<const floatx4*>(blk + (ctq * 64 + lq) * 4);
-                const floatx4 c1 = *reinterpret_cast<const floatx4*>(blk + (ctq * 64 + lq + 16) * 4);
-                u32x4 vh, vm, vl;
+        for (int ks = 0; ks < NCT / 2; ++ks) {
+            const int ctq = 2 * ks + (q4 >> 1);
+            const floatx4 c0 = *reinterpret_cast<const floatx4*>(blk + (ctq * 64 + lq) * 4);
+            const floatx4 c1 = *reinterpret_cast<const floatx4*>(blk + (ctq * 64 + lq + 16) * 4);
+            u32x4 vh, vm, vl;
 #pragma unroll
-                for (int hh = 0; hh < 4; ++hh) {
-                    const floatx4& src = (hh >> 1) ? c1 : c0;
-                    const float x = src[2 * (hh & 1)] * inv, y = src[2 * (hh & 1) + 1] * inv;
-                    const u16 xh = f2bf(x), yh = f2bf(y);
-                    const float xr = x - bf2f(xh), yr = y - bf2f(yh);
-                    const u16 xm = f2bf(xr), ym = f2bf(yr);
-                    vh[hh] = pack2(xh, yh);
-                    vm[hh] = pack2(xm, ym);
-                    vl[hh] = pack2f(xr - bf2f(xm), yr - bf2f(ym));
-                }
-                ub[ks] = as_bf16x8(vh);
-                um[ks] = as_bf16x8(vm);
-                ul[ks] = as_bf16x8(vl);
+            for (int hh = 0; hh < 4; ++hh) {
+                const floatx4& src = (hh >> 1) ? c1 : c0;
+                const float x = src[2 * (hh & 1)] * inv, y = src[2 * (hh & 1) + 1] * inv;
+                const u16 xh = f2bf(x), yh = f2bf(y);
+                const float xr = x - bf2f(xh), yr = y - bf2f(yh);
+                const u16 xm = f2bf(xr), ym = f2bf(yr);
+                vh[hh] = pack2(xh, yh);
+                vm[hh] = pack2(xm, ym);
+                vl[hh] = pack2f(xr - bf2f(xm), yr - bf2f(ym));
             }
-            const int rho = z * R + 16 * rt + r16;
-            const int jrow = (rho % h_q) / hpg;
-            const int first = z * R + 16 * rt;
-            const int jlo = (first % h_q) / hpg, jhi = ((first % h_q) + 15) / hpg;
-            // each lane's row belongs to exactly one group jj of the row tile; its partial
-            // is written in that group's pass
-            for (int jj = jlo; jj <= jhi; ++jj) {
-                // all of the group's weight operands for this wave's columns are loaded
-                // before the first MFMA (one round trip to L2 per row tile and group)
-                const u16* wrow = w_uv + (size_t)jj * DH * RK + VCOLS * vw + (size_t)r16 * RK + q4 * 8;
-                u32x4 wa[DH / 16][NCT / 2];
+            ub[ks] = as_bf16x8(vh);
+            um[ks] = as_bf16x8(vm);
+            ul[ks] = as_bf16x8(vl);
+        }
+        const int rho = z * R + 16 * rt + r16;
+        const int jrow = (rho % h_q) / hpg;
+        const int first = z * R + 16 * rt;
+        const int jlo = (first % h_q) / hpg, jhi = ((first % h_q) + 15) / hpg;
+        // each lane's row belongs to exactly one group jj of the row tile; its partial is
+        // written in that group's pass
+        for (int jj = jlo; jj <= jhi; ++jj) {
+            // all of the group's weight operands for these columns are loaded before the
+            // first MFMA (one round trip to L2 per unit and group)
+            const u16* wrow = w_uv + (size_t)jj * DH * RK + VCOLS * cb + (size_t)r16 * RK + q4 * 8;
+            u32x4 wa[DH / 16][NCT / 2];
 #pragma unroll
-                for (int dt = 0; dt < DH / 16; ++dt)
+            for (int dt = 0; dt < DH / 16; ++dt)
 #pragma unroll
-                    for (int ks = 0; ks < NCT / 2; ++ks)
-                        wa[dt][ks] = *reinterpret_cast<const u32x4*>(wrow + (size_t)dt * 16 * RK + ks * 32);
+                for (int ks = 0; ks < NCT / 2; ++ks)
+                    wa[dt][ks] = *reinterpret_cast<const u32x4*>(wrow + (size_t)dt * 16 * RK + ks * 32);
 #pragma unroll
-                for (int dt = 0; dt < DH / 16; ++dt) {
-                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int dt = 0; dt < DH / 16; ++dt) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < NCT / 2; ++ks) {
-                        acc = mfma16(as_bf16x8(wa[dt][ks]), ub[ks], acc);
-                        acc = mfma16(as_bf16x8(wa[dt][ks]), um[ks], acc);
-                        acc = mfma16(as_bf16x8(wa[dt][ks]), ul[ks], acc);
-                    }
-                    if (jrow == jj) *reinterpret_cast<floatx4*>(blk + (dt * 64 + lane) * 4) = acc;
+                for (int ks = 0; ks < NCT / 2; ++ks) {
+                    acc = mfma16(as_bf16x8(wa[dt][ks]), ub[ks], acc);
+                    acc = mfma16(as_bf16x8(wa[dt][ks]), um[ks], acc);
+                    acc = mfma16(as_bf16x8(wa[dt][ks]), ul[ks], acc);
                 }
+                if (jrow == jj) *reinterpret_cast<floatx4*>(blk + (dt * 64 + lane) * 4) = acc;
             }
         }
-        block_sync();
     }
+    block_sync();   // every unit's partial is written
     // sum the four partials: (row tile, d tile) pairs are dealt round-robin over all waves
     for (int pr_ = wave; pr_ < na * 8; pr_ += NS + NV) {
         const int rt = pr_ >> 3, dt = pr_ & 7;
