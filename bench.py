@@ -13,6 +13,12 @@ group rows with split-K, combine).  The group rows are expanded once per
 sequence beforehand (the method expands the latent once, not per step); that
 expansion is timed on its own and reported as expand_ms.
 
+Before the W warm-up steps the step is run until the GPU's clock has settled
+(reported as "settle"): under this load MI355X's power management first drops the
+SIMD clock to about 1.3 GHz a few launches in and then raises it again over the next
+~50 launches (up to ~1.9 GHz), so a run that starts timing after a few steps
+would measure that transient rather than the steady state.
+
 Prints ONE JSON line: query-tokens/s of the step (batch * s_q / step time),
 per-path times and roofline fractions, the roofline object of the dominant
 kernel (HIP events around that kernel on its own stream) and the fp64 CPU
@@ -60,6 +66,9 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
+    ap.add_argument("--settle-min", type=int, default=120,
+                    help="clock settling: at least this many steps before the warm-up (0: no settling)")
+    ap.add_argument("--settle-max", type=int, default=600, help="clock settling: at most this many steps")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (CPU baseline and its sampled agreement check)")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="flagship",
@@ -258,6 +267,31 @@ def main(argv=None):
     def gqa():
         gqla.decode_gqa(sh, w.q_nope, w.q_rope, gc, w.ctx_lens, out_g, None, ws_g, num_splits=ns_g)
 
+    # clock settling: steps until the step time of the last 20 is within 1 % of the 20
+    # before them (after at least settle_min steps)
+    settle = {"steps": 0, "ms": 0.0, "first_step_ms": None, "last_step_ms": None}
+    if args.settle_min > 0:
+        note("settling clocks")
+        sa, sb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hist = []
+        t_set = time.perf_counter()
+        while True:
+            sa.record()
+            absorb()
+            gqa()
+            sb.record()
+            sb.synchronize()
+            hist.append(sa.elapsed_time(sb))
+            n = len(hist)
+            if n >= max(args.settle_min, 40):
+                prev, last = float(np.mean(hist[-40:-20])), float(np.mean(hist[-20:]))
+                if abs(last - prev) <= 0.01 * last:
+                    break
+            if n >= args.settle_max:
+                break
+        settle = {"steps": len(hist), "ms": round((time.perf_counter() - t_set) * 1e3, 1),
+                  "first_step_ms": round(hist[0], 4), "last_step_ms": round(float(np.mean(hist[-20:])), 4)}
+
     note("warm-up")
     for _ in range(args.warmup):
         absorb()
@@ -361,7 +395,7 @@ def main(argv=None):
         "metric": METRIC,
         "value": round(q_tokens / (ms_per_step * 1e-3), 1),
         "unit": "query-tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "settle": settle,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
