@@ -216,7 +216,7 @@ def main(argv=None):
     import synth
     from latent_kv_cache_amd import gqla
     from latent_kv_cache_amd import roofline as rf
-    from latent_kv_cache_amd.traffic import load_traffic
+    from bench_traffic import load_traffic
     from synth.device import make_workload
 
     dev = torch.device("cuda:0")

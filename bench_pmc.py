@@ -1,6 +1,6 @@
 """Summarise rocprofv3 --pmc CSV output (counter_collection.csv) per kernel.
 
-Usage: python -m latent_kv_cache_amd.pmc_summary <counter_collection.csv> [...]
+Usage: python bench_pmc.py <counter_collection.csv> [...]
 Prints, per kernel name and counter, the mean value per dispatch, and the derived MFMA
 busy fraction, MFMA flops and LDS utilisation when their base counters were collected.
 """

@@ -1,6 +1,6 @@
 """Summarise a rocprofv3 kernel-trace database (rocpd SQLite) as a markdown table.
 
-Usage: python -m latent_kv_cache_amd.profile_summary <results.db> [--command "..."]
+Usage: python bench_profile.py <results.db> [--command "..."]
 Per kernel name: dispatch count, average / min / max duration (us), total (us),
 grid and workgroup sizes, VGPR/AGPR counts and LDS bytes per workgroup.
 """

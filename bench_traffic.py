@@ -7,7 +7,7 @@ counters one hardware pass can collect):
       python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic_WRITE_SIZE -o pmc -- \
       python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
-  python -m latent_kv_cache_amd.traffic \
+  python bench_traffic.py \
       gpurun_out/traffic_FETCH_SIZE/pmc_counter_collection.csv \
       gpurun_out/traffic_WRITE_SIZE/pmc_counter_collection.csv BENCH_LINE_JSON [--write]
 
@@ -28,7 +28,7 @@ import os
 import sys
 from collections import defaultdict
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 RECORDS = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 1 << 30
 
@@ -123,7 +123,7 @@ def summarize(fetch_csv: str, write_csv: str, bench_line: dict):
     note = (f"HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of "
             f"`python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline`, scaled by the counters' reading of "
             f"bench.py's 1 GiB device copy (reads x{read_scale:.3f}, writes x{write_scale:.3f}); written by "
-            f"`python -m latent_kv_cache_amd.traffic`. source_digest: sha256 (16 hex) of each kernel's sources "
+            f"`python bench_traffic.py`. source_digest: sha256 (16 hex) of each kernel's sources "
             f"when the counters were taken.")
     return note, out
 

@@ -8,7 +8,6 @@ no code with the HIP library or its Python binding.
 from .gqla import (  # noqa: F401
     absorb_decode,
     append_rows,
-    decode_batch,
     expand_groups,
     gqa_decode,
     group_of_head,

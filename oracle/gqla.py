@@ -239,34 +239,6 @@ def lse_merge(parts: Sequence[np.ndarray], lses: Sequence[np.ndarray]) -> Tuple[
     return o, lse
 
 
-def decode_batch(form: str, rows_of, q_nope, q_rope, w_uk, w_uv, lengths, scale: float,
-                 seqs=None):
-    """Run one form over a set of sequences.
-
-    form     "textbook" | "absorb" | "gqa"
-    rows_of  callable b -> latent rows of sequence b ([L_b][r_kv + d_R])
-    q_nope / q_rope indexed by position in ``seqs`` (or by b when seqs is None)
-    returns o [n][s_q][h_q][d_h], lse [n][s_q][h_q]
-    """
-    seqs = list(range(len(lengths))) if seqs is None else list(seqs)
-    outs, lses = [], []
-    for n, b in enumerate(seqs):
-        rows = rows_of(b)
-        length = int(lengths[b])
-        if form == "textbook":
-            o, l = textbook_decode(rows, q_nope[n], q_rope[n], w_uk, w_uv, length, scale)
-        elif form == "absorb":
-            o, l = absorb_decode(rows, q_nope[n], q_rope[n], w_uk, w_uv, length, scale)
-        elif form == "gqa":
-            o, l = gqa_decode(expand_groups(rows[:length], w_uk, w_uv), q_nope[n], q_rope[n],
-                              np.asarray(w_uk).shape[0], length, scale)
-        else:
-            raise ValueError(form)
-        outs.append(o)
-        lses.append(l)
-    return np.stack(outs), np.stack(lses)
-
-
 def rope_rotate(x, positions, theta: float = 10000.0) -> np.ndarray:
     """Rotary embedding of vectors x [..., n][d_R] at integer positions [..., n] (float64).
 

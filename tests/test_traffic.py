@@ -3,7 +3,7 @@ averages, on synthetic rocprofv3 CSV rows."""
 import csv
 import json
 
-from latent_kv_cache_amd import traffic
+import bench_traffic as traffic
 
 HEAD = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 
