@@ -142,6 +142,23 @@ def test_edge_lengths(gqla, s_q):
     both_paths(cfg, lens, gqla, 3, max_ctx=96, what=f"edges s_q{s_q}")
 
 
+@pytest.mark.parametrize("batch,seed", [(12, 0), (1040, 1)])
+def test_item_order(gqla, batch, seed):
+    """The GQA grid lists every full chunk first and then the sequences' shorter last
+    chunks, longest first (in sequence order above 1024 sequences).  Lengths mix full
+    chunks, tails of equal length, single rows and empty sequences."""
+    cfg = synth.config(2).with_(batch=batch)
+    rng = np.random.default_rng(7 + seed)
+    if batch <= 16:
+        lens = [700, 256, 300, 556, 44, 300, 0, 512, 44, 699, 1, 257][:batch]
+        max_ctx, splits = 700, 3      # chunks of 256 tokens
+    else:
+        lens = [int(x) for x in rng.integers(0, 97, size=batch)]
+        lens[::7] = [64] * len(lens[::7])
+        max_ctx, splits = 96, 3       # chunks of 32 tokens
+    both_paths(cfg, lens, gqla, splits, max_ctx=max_ctx, what=f"order B{batch}")
+
+
 def test_chunk_boundary_causal(gqla):
     """s_q = 2 with L - 1 on a chunk boundary: query 0 sees nothing of the last chunk."""
     cfg = synth.config(4, s_q=2).with_(batch=2)
