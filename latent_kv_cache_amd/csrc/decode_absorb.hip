@@ -309,11 +309,16 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
     const int z = slot % nz;
     const int pair = (slot / nz) * 8 + xcd;
     if (pair >= n_split * batch) return;           // padding of the last group of 8
-    // pair = p * batch + bb with b = (bb + p) mod batch: the sequence index varies fastest
-    // across XCDs and chunk p of sequence b runs on XCD (b + p) % 8, so ragged batches
-    // spread evenly
-    const int p = pair / batch, bb = pair - p * batch;
-    const int b = bb + p % batch < batch ? bb + p % batch : bb + p % batch - batch;
+    // One chunk per sequence: item k is sequence k.  Several: the items are ordered
+    // longest first (chunk_of_item), so the short last chunks of a ragged batch fill in
+    // at the end.
+    int b = pair, p = 0;
+    if (n_split > 1) {
+        if (!chunk_of_item<(NS + NV) * 64>(pair, ctx_lens, batch, max_ctx, chunk,
+                                           reinterpret_cast<int*>(lds.tiles[0]), b, p))
+            return;
+        __syncthreads();   // the item is known to every thread before the tiles reuse LDS
+    }
     const int L = clampi(ctx_lens[b], 0, max_ctx);
     const int t0 = p * chunk;
     const int RQ = s_q * h_q;

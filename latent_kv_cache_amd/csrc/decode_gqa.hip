@@ -135,96 +135,6 @@ __device__ __forceinline__ void store_tile(u16* lds, const u32x4 (&reg)[NLOAD], 
 }
 
 // ---------------------------------------------------------------------------
-// Order of the work items (the (sequence, chunk) pairs) over the grid: every full chunk
-// first, sequence by sequence, then the sequences' shorter last chunks, longest first.
-// The dispatcher hands blocks to compute units in grid order as they free up, so the
-// long items start first and the short ones fill in at the end, which keeps ragged
-// batches from ending on a few CUs that still stream whole chunks.  Batches above
-// kSortTails sequences keep their last chunks in sequence order.
-// chunk_of_item maps item k to (sequence b, chunk p); false when k is past the last
-// item.  Every thread of the block calls it with the same k.  sh: LDS scratch of at
-// least max(min(batch, kSortTails) + 1, NT / 64 + 2) ints (the tile buffer, before its
-// first use).
-// ---------------------------------------------------------------------------
-constexpr int kSortTails = 1024;
-
-template <int NT>
-__device__ __forceinline__ bool chunk_of_item(int k, const int32_t* __restrict__ ctx_lens, int batch, int max_ctx,
-                                              int chunk, int* sh, int& b_out, int& p_out) {
-    constexpr int NWV = NT / 64;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    auto len_of = [&](int b) { return clampi(ctx_lens[b], 0, max_ctx); };
-    // Block-wide exclusive scan of v(b) over the batch: the one thread whose b has v > 0
-    // and holds position k' in [excl, excl + v) stores b and k' - excl at sh[NWV],
-    // sh[NWV + 1].  Returns the total.
-    auto scan_find = [&](auto v_of, int kk) -> int {
-        int run = 0;
-        for (int base = 0; base < batch; base += NT) {
-            const int b = base + tid;
-            const int v = b < batch ? v_of(b) : 0;
-            int x = v;   // inclusive scan over the wave
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o);
-                if (lane >= o) x += y;
-            }
-            if (lane == 63) sh[wv] = x;
-            __syncthreads();
-            int woff = 0, ctot = 0;
-#pragma unroll
-            for (int i = 0; i < NWV; ++i) {
-                woff += i < wv ? sh[i] : 0;
-                ctot += sh[i];
-            }
-            const int excl = run + woff + x - v;
-            __syncthreads();
-            if (v > 0 && excl <= kk && kk < excl + v) {
-                sh[NWV] = b;
-                sh[NWV + 1] = kk - excl;
-            }
-            run += ctot;
-        }
-        __syncthreads();
-        return run;
-    };
-    // full chunks: floor(L_b / chunk) per sequence
-    const int nfull = scan_find([&](int b) { return len_of(b) / chunk; }, k);
-    if (k < nfull) {
-        b_out = sh[NWV];
-        p_out = sh[NWV + 1];
-        return true;
-    }
-    const int i = k - nfull;   // rank of the wanted last chunk
-    __syncthreads();           // sh[NWV], sh[NWV + 1] are read before sh is reused
-    int found;
-    if (batch <= kSortTails) {
-        // a last chunk's rank: the number of longer ones plus the equal ones before it
-        for (int b = tid; b < batch; b += NT) sh[b] = len_of(b) % chunk;
-        if (tid == 0) sh[batch] = -1;
-        __syncthreads();
-        for (int b = tid; b < batch; b += NT) {
-            const int r = sh[b];
-            if (r == 0) continue;
-            int rank = 0;
-            for (int c = 0; c < batch; ++c) {
-                const int rc = sh[c];
-                rank += (rc > r) || (rc == r && c < b);
-            }
-            if (rank == i) sh[batch] = b;   // outside the range the other threads read
-        }
-        __syncthreads();
-        found = sh[batch];
-    } else {
-        const int ntail = scan_find([&](int b) { return len_of(b) % chunk ? 1 : 0; }, i);
-        found = i < ntail ? sh[NWV] : -1;
-    }
-    if (found < 0) return false;   // past the last item
-    b_out = found;
-    p_out = len_of(found) / chunk;
-    return true;
-}
-
-// ---------------------------------------------------------------------------
 // GQA decode.  One-dimensional XCD-aware grid; block = NW waves.  Block id i runs on
 // XCD i % 8; its slot i / 8 gives the pair block z = slot % nz and the (sequence,
 // chunk) unit u = (slot / nz) * 8 + i % 8 = p * batch + bb, sequence b = (bb + p) mod
