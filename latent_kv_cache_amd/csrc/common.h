@@ -211,4 +211,42 @@ __device__ __forceinline__ bool chunk_of_item(int k, const int32_t* __restrict__
     return true;
 }
 
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane l's
+// bytes land at LDS byte address lds_base + 16 l; lds_base must be wave-uniform.  It is
+// issued from inline assembly so that the compiler, which cannot tell which LDS bytes
+// such a load writes, does not wait for all of them before every later LDS access;
+// callers wait with wait_vmcnt<> before reading the destination.  The compiler does not
+// count these loads, so its own waits on later global loads only over-wait (loads
+// retire in issue order).  The global address is a wave-uniform 64-bit base (SGPRs)
+// plus a 32-bit per-lane byte offset.  Lanes outside EXEC write nothing.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt immediate on gfx9: vmcnt = bits [3:0] and [15:14]; expcnt and
+    // lgkmcnt fields left at their maxima (no wait on them)
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Barrier without the compiler's memory fence (whose vmcnt(0) would drain the direct
+// loads still in flight): own LDS operations complete, then s_barrier.
+__device__ __forceinline__ void block_sync() {
+    asm volatile("" ::: "memory");
+    // s_waitcnt lgkmcnt(0): vmcnt field at its maximum 63 (bits [3:0] and [15:14]),
+    // expcnt at 7, lgkmcnt (bits [11:8]) at 0
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace gqla

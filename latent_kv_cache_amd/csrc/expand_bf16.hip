@@ -10,10 +10,11 @@
 //
 // Tiling.  A block covers 256 output columns of 2048 tokens of one sequence; each of its
 // 8 waves owns 32 output columns and keeps their 32 x 512 weight rows in registers as
-// two MFMA A operands for the whole block; 64-token latent tiles are staged in LDS
+// two MFMA A operands for the whole block; 32-token latent tiles are staged in LDS
 // (32-byte row pad, bank-conflict free) and read as the B operand.
 //   out^T[col][token] = W[col][r] . c^T[r][token]
-// so lane (q, r16) ends with 4 consecutive columns of token r16: 8-byte stores.
+// so lane (q, r16) ends with 4 consecutive columns of token r16; these are staged in LDS
+// and leave as 16-byte stores that write whole 512-byte row segments.
 #include "common.h"
 #include "launch.h"
 
@@ -27,23 +28,49 @@ constexpr int XSTRIDE = RK + 16;        // LDS row stride of a staged latent til
 
 // Block = 8 waves x 32 output columns (256 columns) x 2048 tokens.  A wave keeps the 32
 // weight rows of its columns in registers (two 16-row A operands) for the whole block,
-// so each 16-byte latent operand read from LDS feeds two MFMAs; the next 64-token tile
-// is loaded into registers while the current one is multiplied.
+// so each 16-byte latent operand read from LDS feeds two MFMAs.
 // One-dimensional, XCD-aware grid: the 2g d_h / 256 column blocks of one token chunk get
 // ids 8 apart, so they run on one XCD and all but the first read the chunk's latent
 // rows from that XCD's L2 instead of HBM.
+// Steps of ET tokens over three input and two output LDS buffers.  At step k, after the
+// barrier that published input tile k:
+//   - the latent rows of tile k+2 go from global memory straight into an input buffer
+//     (global_load_lds_dwordx4, one wave instruction per 1 KB row), so every load has
+//     two steps to land;
+//   - the MFMAs of tile k run, and between them every thread stores two 16-byte pieces
+//     of tile k-1's output from output buffer (k-1)%2 (each wave instruction writes two
+//     whole 512-byte row segments);
+//   - the MFMA results of tile k are written to output buffer k%2;
+//   - each wave waits for its loads of tile k+1 (not for anything issued after them),
+//     then the barrier.
+// The first column block also copies the rotary keys, staged through LDS with the tile.
 constexpr int XCOLS = 256;              // output columns per block
-constexpr int XTOK_BLOCK = 2048;        // tokens per block (32 tiles)
+constexpr int OSTRIDE = XCOLS + 8;      // LDS row stride of a staged output tile
+constexpr int XTOK_BLOCK = 2048;        // tokens per block
+constexpr int ET = 32;                  // tokens per step
+constexpr int NIB = 3;                  // input buffers
+constexpr int EPF = 3;                  // k-steps an LDS operand read runs ahead of its MFMAs
+constexpr int EXW = 8;                  // waves per block (32 columns each)
 
-template <int G>
-__global__ __launch_bounds__(512) void expand_kernel(
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64) void expand_kernel(
     const u16* __restrict__ latent, int64_t lbs, const u16* __restrict__ w_uk, const u16* __restrict__ w_uv,
     const int32_t* __restrict__ ctx_lens, int max_ctx, int row_begin, int batch, int n_chunks,
     u16* __restrict__ gc, int64_t gbs) {
+    constexpr int NT = NW * 64;                  // threads
+    constexpr int CT = XCOLS / 16 / NW;          // 16-column MFMA tiles per wave
+    constexpr int RPW = ET / NW;                 // latent rows each wave loads per tile
+    constexpr int RLN = ET * (DR / 8) / NW;      // lanes per wave that load / store rotary keys
+    constexpr int EST = ET * (XCOLS / 8) / NT;   // 16-byte output stores per thread per step
+    constexpr int KS = RK / 32;                  // k-steps
+    static_assert(RLN <= 64 && RPW * NW == ET && EST * NT == ET * (XCOLS / 8), "tile shape");
     constexpr int WOUT = 2 * G * DH + DR;
     constexpr int WIN = RK + DR;
-    constexpr int NST = XT * (RK / 8) / 512;   // 16-byte chunks per thread per tile
-    __shared__ __attribute__((aligned(16))) u16 lds[2 * XT * XSTRIDE];
+    constexpr int ITILE = ET * XSTRIDE, RTILE = ET * DR, OTILE = ET * OSTRIDE;   // u16 elements
+    __shared__ __attribute__((aligned(16))) u16 lds[NIB * (ITILE + RTILE) + 2 * OTILE];
+    auto ibuf = [&](int i) -> u16* { return lds + i * ITILE; };
+    auto rbuf = [&](int i) -> u16* { return lds + NIB * ITILE + i * RTILE; };
+    auto obuf = [&](int k) -> u16* { return lds + NIB * (ITILE + RTILE) + (k & 1) * OTILE; };
 
     constexpr int NCB = 2 * G * DH / XCOLS;    // column blocks
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -61,97 +88,135 @@ __global__ __launch_bounds__(512) void expand_kernel(
     const int tend = min(tbeg + XTOK_BLOCK, L);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q4 = lane >> 4, r16 = lane & 15;
-    const int col0 = cb * XCOLS + wave * 32;   // first output column of this wave
-    auto wrow = [&](int col) {
-        return col < G * DH ? w_uk + (size_t)col * RK : w_uv + (size_t)(col - G * DH) * RK;
-    };
-    const u16* w0 = wrow(col0 + r16);
-    const u16* w1 = wrow(col0 + 16 + r16);
-    bf16x8 wa0[RK / 32], wa1[RK / 32];
+    const bool rope = cb == 0;
+    const int col0 = cb * XCOLS + wave * CT * 16;   // first output column of this wave
+    bf16x8 wa[CT][KS];
 #pragma unroll
-    for (int ks = 0; ks < RK / 32; ++ks) {
-        wa0[ks] = ld_bf16x8(w0 + ks * 32 + q4 * 8);
-        wa1[ks] = ld_bf16x8(w1 + ks * 32 + q4 * 8);
+    for (int ct = 0; ct < CT; ++ct) {
+        const int col = col0 + ct * 16 + r16;
+        const u16* w = col < G * DH ? w_uk + (size_t)col * RK : w_uv + (size_t)(col - G * DH) * RK;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) wa[ct][ks] = ld_bf16x8(w + ks * 32 + q4 * 8);
     }
 
     const u16* src = latent + (size_t)b * lbs;
     u16* dst = gc + (size_t)b * gbs;
-    // latent rows of a tile: chunk c = k*512 + tid is row c/64, columns 8(c%64)..; rows past
-    // the block's end load its last row (in bounds, results not stored)
-    u32x4 st[NST];
-    auto load_tile = [&](int tb) {
+    // Tile tb into input buffer i: wave w loads rows w, w + NW, ..; rows past the block's
+    // end load its last row (in bounds, results not stored).  With the rotary keys, lanes
+    // 0..RLN-1 of wave w also load those of rows w RLN / 8 .. into the tile's rope area.
+    // Loads per wave: RPW, plus one with the rotary keys.
+    const int rr = wave * (RLN / 8) + (lane >> 3), rc = (lane & 7) * 8;   // rotary row and column
+    auto load_tile = [&](int tb, int i) {
         const int last = tend - 1 - tb;
+        const uint32_t lb = lds_addr(ibuf(i));
 #pragma unroll
-        for (int k = 0; k < NST; ++k) {
-            const int c = k * 512 + tid;
-            st[k] = *reinterpret_cast<const u32x4*>(src + (size_t)(tb + min(c >> 6, last)) * WIN + (c & 63) * 8);
+        for (int k = 0; k < RPW; ++k) {
+            const int r = k * NW + wave;
+            dma16(src + (size_t)(tb + min(r, last)) * WIN, (uint32_t)lane * 16u, lb + (uint32_t)(r * XSTRIDE * 2));
         }
+        if (rope && lane < RLN)
+            dma16(src + (size_t)tb * WIN + RK, (uint32_t)(min(rr, last) * WIN + rc) * 2u,
+                  lds_addr(rbuf(i) + wave * (RLN / 8) * DR));
     };
-    // two LDS tiles: the next tile is stored into the other buffer after this one's
-    // MFMAs, so one barrier per tile suffices
-    auto store_tile = [&](u16* buf) {
-#pragma unroll
-        for (int k = 0; k < NST; ++k) {
-            const int c = k * 512 + tid;
-            *reinterpret_cast<u32x4*>(buf + (c >> 6) * XSTRIDE + (c & 63) * 8) = st[k];
-        }
+    // Piece j (< EST) of this thread's share of a staged output tile: row r, 8 columns.
+    // Read from LDS well before the store, so that the store does not wait for every LDS
+    // read in flight (LDS operations complete in order).
+    auto piece_row = [&](int j) { return (j * NT + tid) / (XCOLS / 8); };
+    auto piece_col = [&](int j) { return ((j * NT + tid) % (XCOLS / 8)) * 8; };
+    auto read_piece = [&](const u16* ob, int j) {
+        return *reinterpret_cast<const u32x4*>(ob + piece_row(j) * OSTRIDE + piece_col(j));
     };
-    load_tile(tbeg);
-    store_tile(lds);
-    __syncthreads();
-    for (int tb = tbeg, it = 0; tb < tend; tb += XT, ++it) {
-        const int nr = min(XT, tend - tb);
-        const u16* cur = lds + (it & 1) * (XT * XSTRIDE);
-        // the first column block also copies the rotary keys
-        if (cb == 0) {
-            for (int c = tid; c < nr * (DR / 8); c += 512) {
-                const int r = c >> 3, col = c & 7;
-                *reinterpret_cast<u32x4*>(dst + (size_t)(tb + r) * WOUT + 2 * G * DH + col * 8) =
-                    *reinterpret_cast<const u32x4*>(src + (size_t)(tb + r) * WIN + RK + col * 8);
-            }
+    auto store_piece = [&](u32x4 v, int tb, int nr, int j) {
+        const int r = piece_row(j);
+        if (r < nr)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + (size_t)(tb + r) * WOUT + cb * XCOLS + piece_col(j)));
+    };
+    const int ntiles = (tend - tbeg + ET - 1) / ET;
+    load_tile(tbeg, 0);
+    if (ntiles > 1) load_tile(tbeg + ET, 1);
+    // the compiler does not count the direct loads, and a workgroup barrier does not wait
+    // for vector memory: each wave waits for its own loads, then the barrier
+    wait_vmcnt<0>();
+    block_sync();
+    int ptb = 0, pnr = 0;   // the previous tile, whose output is stored during this step
+    for (int it = 0, bi = 0; it < ntiles; ++it, bi = bi == NIB - 1 ? 0 : bi + 1) {
+        const int tb = tbeg + it * ET, nr = min(ET, tend - tb);
+        const bool more2 = it + 2 < ntiles;
+        // tile it+2 into the buffer that tile it-1 used
+        if (more2) load_tile(tb + 2 * ET, bi == 0 ? NIB - 1 : bi - 1);
+        const u16* cur = ibuf(bi);
+        // tile it-1's output, staged in output buffer (it-1)%2, and this tile's rotary keys
+        u32x4 pv[EST], rv;
+        if (it > 0) {
+#pragma unroll
+            for (int j = 0; j < EST; ++j) pv[j] = read_piece(obuf(it + 1), j);
         }
-        if (tb + XT < tend) load_tile(tb + XT);
-        // two 16-token tiles at a time: four independent accumulator chains per wave
+        if (rope && lane < RLN) rv = *reinterpret_cast<const u32x4*>(rbuf(bi) + rr * DR + rc);
+        // two 16-token halves: 2 CT independent accumulator chains per wave
+        floatx4 acc[2][CT] = {};
+        const u16* brow = cur + r16 * XSTRIDE + q4 * 8;
+        bf16x8 bq[EPF][2];
 #pragma unroll
-        for (int np = 0; np < XT / 32; ++np) {
-            floatx4 acc[2][2] = {};
-            const u16* brow = cur + (np * 32 + r16) * XSTRIDE + q4 * 8;
-            // operands read three k-steps ahead of their MFMAs (LDS latency)
-            constexpr int PF = 3;
-            bf16x8 bq[PF][2];
-#pragma unroll
-            for (int ks = 0; ks < PF; ++ks) {
-                bq[ks][0] = ld_bf16x8(brow + ks * 32);
-                bq[ks][1] = ld_bf16x8(brow + 16 * XSTRIDE + ks * 32);
-            }
-#pragma unroll
-            for (int ks = 0; ks < RK / 32; ++ks) {
-                const bf16x8 b0 = bq[ks % PF][0], b1 = bq[ks % PF][1];
-                if (ks + PF < RK / 32) {
-                    bq[ks % PF][0] = ld_bf16x8(brow + (ks + PF) * 32);
-                    bq[ks % PF][1] = ld_bf16x8(brow + 16 * XSTRIDE + (ks + PF) * 32);
-                }
-                acc[0][0] = mfma16(wa0[ks], b0, acc[0][0]);
-                acc[0][1] = mfma16(wa1[ks], b0, acc[0][1]);
-                acc[1][0] = mfma16(wa0[ks], b1, acc[1][0]);
-                acc[1][1] = mfma16(wa1[ks], b1, acc[1][1]);
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int tok = np * 32 + h * 16 + r16;
-                if (tok < nr) {
-                    u16* o = dst + (size_t)(tb + tok) * WOUT + col0 + q4 * 4;
-                    *reinterpret_cast<u32x2*>(o) = u32x2{pack2f(acc[h][0][0], acc[h][0][1]), pack2f(acc[h][0][2], acc[h][0][3])};
-                    *reinterpret_cast<u32x2*>(o + 16) =
-                        u32x2{pack2f(acc[h][1][0], acc[h][1][1]), pack2f(acc[h][1][2], acc[h][1][3])};
-                }
-            }
+        for (int ks = 0; ks < EPF; ++ks) {
+            bq[ks][0] = ld_bf16x8(brow + ks * 32);
+            bq[ks][1] = ld_bf16x8(brow + 16 * XSTRIDE + ks * 32);
         }
-        if (tb + XT < tend) store_tile(lds + ((it + 1) & 1) * (XT * XSTRIDE));
-        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 b0 = bq[ks % EPF][0], b1 = bq[ks % EPF][1];
+            if (ks + EPF < KS) {
+                bq[ks % EPF][0] = ld_bf16x8(brow + (ks + EPF) * 32);
+                bq[ks % EPF][1] = ld_bf16x8(brow + 16 * XSTRIDE + (ks + EPF) * 32);
+            }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                acc[0][ct] = mfma16(wa[ct][ks], b0, acc[0][ct]);
+                acc[1][ct] = mfma16(wa[ct][ks], b1, acc[1][ct]);
+            }
+            if (it > 0 && ks % (KS / EST) == KS / EST / 2) store_piece(pv[ks / (KS / EST)], ptb, pnr, ks / (KS / EST));
+            if (ks == 1 && rope && lane < RLN && rr < nr)   // one rotary store per wave
+                __builtin_nontemporal_store(rv, reinterpret_cast<u32x4*>(dst + (size_t)(tb + rr) * WOUT + 2 * G * DH + rc));
+            // keeps each k-step's reads EPF steps ahead of their MFMAs (left to itself the
+            // scheduler moves every read next to its MFMAs)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // this tile's results into output buffer it%2 (its previous contents, tile it-2,
+        // were stored during step it-1)
+        u16* const ob = obuf(it);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                *reinterpret_cast<u32x2*>(ob + (h * 16 + r16) * OSTRIDE + wave * CT * 16 + ct * 16 + q4 * 4) =
+                    u32x2{pack2f(acc[h][ct][0], acc[h][ct][1]), pack2f(acc[h][ct][2], acc[h][ct][3])};
+        ptb = tb;
+        pnr = nr;
+        // This wave's loads of tile it+1 have landed.  Vector memory operations complete
+        // in issue order.  Issued after those loads (at the start of step it-1, before
+        // the loop for it = 0), and left in flight, are: the stores of step it-1 (EST
+        // from step 2 on, and the rope store), the loads of tile it+2 (RPW, and the
+        // rope load), and the stores of this step (likewise).  Every tile stored here is
+        // full, so no store is skipped; the last tile needs no wait.  Rope blocks
+        // over-wait where the counts below leave out their rope operations.
+        if (it + 1 < ntiles) {
+            if (it == 0)
+                wait_vmcnt<0>();
+            else if (it == 1)
+                more2 ? wait_vmcnt<EST + RPW>() : wait_vmcnt<EST>();
+            else if (!more2)
+                wait_vmcnt<2 * EST>();
+            else if (rope)
+                wait_vmcnt<2 * (EST + 1) + RPW + 1>();
+            else
+                wait_vmcnt<2 * EST + RPW>();
+        }
+        block_sync();   // every wave's have, tile it is read and its output staged
     }
+    // the last tile's output
+#pragma unroll
+    for (int j = 0; j < EST; ++j) store_piece(read_piece(obuf(ntiles - 1), j), ptb, pnr, j);
 }
 
 // Expansion of the decode step's new rows (the append): row r < batch * s_q of c_new
@@ -231,7 +296,7 @@ hipError_t launch_expand_g(const ExpandArgs& a, hipStream_t st) {
     const int cps = (span + XTOK_BLOCK - 1) / XTOK_BLOCK;
     const int n_chunks = cps * a.batch;
     dim3 grid(((n_chunks + 7) / 8) * 8 * (2 * G * DH / XCOLS));
-    hipLaunchKernelGGL(expand_kernel<G>, grid, dim3(512), 0, st, (const u16*)a.latent, a.latent_bstride,
+    hipLaunchKernelGGL((expand_kernel<G, EXW>), grid, dim3(EXW * 64), 0, st, (const u16*)a.latent, a.latent_bstride,
                        (const u16*)a.w_uk, (const u16*)a.w_uv, a.ctx_lens, a.max_ctx, a.row_begin, a.batch, n_chunks,
                        (u16*)a.group_cache, a.group_bstride);
     return hipGetLastError();
