@@ -151,10 +151,11 @@ Plan plan(const gqla_shape& s, int path, int batch, int max_ctx, int num_splits)
 // Length-aware choice of num_splits (bf16 absorb and GQA paths).  A decode launch is
 // a grid of workgroups, one per (context chunk, sequence) pair and, on the absorb
 // path, per 128-row group of query rows.  Workgroups of pairs past a sequence's end
-// return at once.  The candidates are the automatic plan and the "fill" plans whose
-// grid is exactly k times the concurrent workgroups of the device (k = 1..4), so that
-// no round of workgroups is partly filled; the estimate of a plan is
-//   rounds x (min(chunk, longest context) + overhead),
+// return at once.  The candidates are the automatic plan, the "fill" plans whose grid
+// is exactly k times the concurrent workgroups of the device, and the balanced plans
+// with the smallest chunk whose non-empty workgroups fit k rounds (k = 1..4); the
+// estimate of a plan is
+//   rounds x (longest work item + overhead),
 // rounds = ceil(non-empty workgroups / concurrent workgroups), with the per-workgroup
 // overhead (query staging, the W_UV epilogue or output write, the partial it adds to
 // the combine) in tokens: about 1000, fitted on MI355X to the absorb kernel on the
@@ -168,16 +169,29 @@ Plan plan(const gqla_shape& s, int path, int batch, int max_ctx, int num_splits)
 // so one crowded group of CUs sets the time: measured at 16 sequences of 64K-128K
 // tokens, 18-22 chunks per sequence (288-352 workgroups for 256 CUs, a quarter of them
 // empty) ran 30-60 % slower than 16 chunks (256 workgroups).
-double split_estimate(const int32_t* lens, int batch, int max_ctx, int chunk, int mult, int slots, double ovh) {
+// Work items of a plan with chunk c: sequence b gives ceil(L_b / c) items of
+// roundup32(ceil(L_b / n)) tokens (the kernels' equal per-sequence chunks).
+long long split_items(const int32_t* lens, int batch, int max_ctx, int chunk, int mult, int* longest_item) {
     long long units = 0;
     int longest = 0;
     for (int b = 0; b < batch; ++b) {
         const int L = std::min(std::max(lens[b], 0), max_ctx);
-        units += (long long)mult * ((L + chunk - 1) / chunk);
-        longest = std::max(longest, L);
+        const int n = (L + chunk - 1) / chunk;
+        units += (long long)mult * n;
+        if (n > 0) {
+            const int a = gqla::kBf16TokenTile;
+            longest = std::max(longest, ((L + n - 1) / n + a - 1) / a * a);
+        }
     }
+    if (longest_item) *longest_item = longest;
+    return units;
+}
+
+double split_estimate(const int32_t* lens, int batch, int max_ctx, int chunk, int mult, int slots, double ovh) {
+    int longest = 0;
+    const long long units = split_items(lens, batch, max_ctx, chunk, mult, &longest);
     const long long rounds = (units + slots - 1) / slots;
-    return (double)rounds * (std::min(chunk, longest) + ovh);
+    return (double)rounds * (longest + ovh);
 }
 
 struct Layout {
@@ -296,6 +310,7 @@ gqla_status decode_common(int path, const gqla_shape* sp, int32_t batch, int32_t
     a.max_ctx = max_ctx;
     a.n_split = p.n_split;
     a.chunk = p.chunk;
+    a.cus = device_cus();
     a.q_nope = q_nope;
     a.q_rope = q_rope;
     a.w_uk = w_uk;
@@ -383,7 +398,7 @@ gqla_status gqla_plan_splits_lens(const gqla_shape* shape, int32_t path, int32_t
         // a small share of the time and the automatic plan stands
         if (auto_units < 4LL * slots) {
             // candidates (num_splits argument, chunks per sequence), fewest chunks first
-            int cand_w[5], cand_n[5], nc = 0;
+            int cand_w[9], cand_n[9], nc = 0;
             const long long fill = slots / ((long long)batch * mult);   // chunks per sequence, one round
             for (int k = 1; fill > 0 && k <= 4; ++k) {
                 const int w = (int)(k * fill);
@@ -392,6 +407,26 @@ gqla_status gqla_plan_splits_lens(const gqla_shape* shape, int32_t path, int32_t
                 if ((long long)pl.n_split * batch * mult > (long long)k * slots) continue;
                 cand_w[nc] = w;
                 cand_n[nc++] = pl.n_split;
+            }
+            // balanced plans: the smallest chunk whose work items (empty chunks of short
+            // sequences are no items) fit k rounds; items of one sequence are of equal
+            // size, so with ragged lengths these fill the rounds more evenly than a grid
+            // of k rounds of chunks
+            const int w_max = std::max(1, (max_ctx + gqla::kBf16TokenTile - 1) / gqla::kBf16TokenTile);
+            for (int k = 1; k <= 4; ++k) {
+                auto fits = [&](int w) {
+                    return split_items(host_ctx_lens, batch, max_ctx, plan(s, path, batch, max_ctx, w).chunk, mult,
+                                       nullptr) <= (long long)k * slots;
+                };
+                if (!fits(1)) continue;
+                int lo = 1, hi = w_max;   // fits(lo); largest w that fits
+                while (lo < hi) {
+                    const int mid = lo + (hi - lo + 1) / 2;
+                    if (fits(mid)) lo = mid;
+                    else hi = mid - 1;
+                }
+                cand_w[nc] = lo;
+                cand_n[nc++] = plan(s, path, batch, max_ctx, lo).n_split;
             }
             cand_w[nc] = 0;
             cand_n[nc++] = plan(s, path, batch, max_ctx, 0).n_split;

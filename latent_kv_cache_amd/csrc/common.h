@@ -122,33 +122,49 @@ __device__ __forceinline__ float wave_sum16x4(float v) {
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // ---------------------------------------------------------------------------
-// Order of the work items (the (sequence, chunk) pairs) over the grid: every full chunk
-// first, sequence by sequence, then the sequences' shorter last chunks, longest first.
-// The dispatcher hands blocks to compute units in grid order as they free up, so the
-// long items start first and the short ones fill in at the end, which keeps ragged
-// batches from ending on a few CUs that still stream whole chunks.  Batches above
-// kSortTails sequences keep their last chunks in sequence order.
-// chunk_of_item maps item k to (sequence b, chunk p); false when k is past the last
-// item.  Every thread of the block calls it with the same k.  sh: LDS scratch of at
-// least max(min(batch, kSortTails) + 1, NT / 64 + 2) ints (the tile buffer, before its
-// first use).
+// Split-K work items.  With the planned chunk c (a multiple of the 32-token tile),
+// sequence b of length L gives n = ceil(L / c) items, the chunks whose partials the
+// combine merges.  How the n chunks cut the sequence, and the order of the items over
+// the grid, depend on whether all items of the launch run at once (at most `cap`
+// items, the concurrent workgroups of the device divided by the workgroups per item):
+// - One round: the chunks of a sequence are of equal size, cb = ceil(L / n) rounded up
+//   to a multiple of 32 (cb <= c, and ceil(L / cb) = n), the last one the rest, in
+//   sequence order.  A ragged batch then has no short last chunks: all items are
+//   between about c (n - 1) / n and c tokens, and the planner can pick c so that they
+//   fill the compute units evenly.
+// - Several rounds: chunks of c tokens and a shorter last one; every full chunk first,
+//   sequence by sequence, then the last chunks, longest first.  The dispatcher hands
+//   blocks to compute units in grid order as they free up, so the long items start
+//   first and the short ones fill the last round in.
+// Batches above kSortTails sequences keep their last chunks in sequence order.
+// chunk_of_item maps item k to (sequence b, chunk p, tokens [t0, t1)); false when k is
+// past the last item.  Every thread of the block calls it with the same k.  sh: LDS
+// scratch of at least NT / 64 + 2 + 2 min(batch, kSortTails) ints (the tile buffer,
+// before its first use).
 // ---------------------------------------------------------------------------
 constexpr int kSortTails = 1024;
+constexpr int kChunkAlign = 32;
+
+__device__ __forceinline__ int chunks_of(int L, int chunk) { return (L + chunk - 1) / chunk; }
+__device__ __forceinline__ int chunk_size(int L, int n) {
+    return ((L + n - 1) / n + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+}
 
 template <int NT>
 __device__ __forceinline__ bool chunk_of_item(int k, const int32_t* __restrict__ ctx_lens, int batch, int max_ctx,
-                                              int chunk, int* sh, int& b_out, int& p_out) {
+                                              int chunk, int cap, int* sh, int& b_out, int& p_out, int& t0_out,
+                                              int& t1_out) {
     constexpr int NWV = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     auto len_of = [&](int b) { return clampi(ctx_lens[b], 0, max_ctx); };
-    // Block-wide exclusive scan of v(b) over the batch: the one thread whose b has v > 0
-    // and holds position k' in [excl, excl + v) stores b and k' - excl at sh[NWV],
+    // Block-wide exclusive scan of v(i) over i < batch: the one thread whose i has v > 0
+    // and holds position kk in [excl, excl + v) stores i and kk - excl at sh[NWV],
     // sh[NWV + 1].  Returns the total.
     auto scan_find = [&](auto v_of, int kk) -> int {
         int run = 0;
         for (int base = 0; base < batch; base += NT) {
-            const int b = base + tid;
-            const int v = b < batch ? v_of(b) : 0;
+            const int i = base + tid;
+            const int v = i < batch ? v_of(i) : 0;
             int x = v;   // inclusive scan over the wave
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -159,14 +175,14 @@ __device__ __forceinline__ bool chunk_of_item(int k, const int32_t* __restrict__
             __syncthreads();
             int woff = 0, ctot = 0;
 #pragma unroll
-            for (int i = 0; i < NWV; ++i) {
-                woff += i < wv ? sh[i] : 0;
-                ctot += sh[i];
+            for (int w = 0; w < NWV; ++w) {
+                woff += w < wv ? sh[w] : 0;
+                ctot += sh[w];
             }
             const int excl = run + woff + x - v;
             __syncthreads();
             if (v > 0 && excl <= kk && kk < excl + v) {
-                sh[NWV] = b;
+                sh[NWV] = i;
                 sh[NWV + 1] = kk - excl;
             }
             run += ctot;
@@ -174,40 +190,55 @@ __device__ __forceinline__ bool chunk_of_item(int k, const int32_t* __restrict__
         __syncthreads();
         return run;
     };
-    // full chunks: floor(L_b / chunk) per sequence
-    const int nfull = scan_find([&](int b) { return len_of(b) / chunk; }, k);
-    if (k < nfull) {
-        b_out = sh[NWV];
-        p_out = sh[NWV + 1];
+    const bool sorted = batch <= kSortTails;
+    int* key = sh + NWV + 2;   // per sequence: last-chunk length
+    int* perm = key + batch;   // sequences by decreasing key, ties in sequence order
+
+    // all items in sequence order; the total decides between one round and several
+    const int total = scan_find([&](int b) { return chunks_of(len_of(b), chunk); }, k);
+    if (k >= total) return false;   // past the last item
+    if (total <= cap) {
+        // every item starts at once, so their order does not matter
+        const int b = sh[NWV];
+        const int p = sh[NWV + 1];
+        const int L = len_of(b), cb = chunk_size(L, chunks_of(L, chunk));
+        b_out = b;
+        p_out = p;
+        t0_out = p * cb;
+        t1_out = min(t0_out + cb, L);
         return true;
     }
-    const int i = k - nfull;   // rank of the wanted last chunk
-    __syncthreads();           // sh[NWV], sh[NWV + 1] are read before sh is reused
-    int found;
-    if (batch <= kSortTails) {
-        // a last chunk's rank: the number of longer ones plus the equal ones before it
-        for (int b = tid; b < batch; b += NT) sh[b] = len_of(b) % chunk;
-        if (tid == 0) sh[batch] = -1;
-        __syncthreads();
-        for (int b = tid; b < batch; b += NT) {
-            const int r = sh[b];
-            if (r == 0) continue;
-            int rank = 0;
-            for (int c = 0; c < batch; ++c) {
-                const int rc = sh[c];
-                rank += (rc > r) || (rc == r && c < b);
-            }
-            if (rank == i) sh[batch] = b;   // outside the range the other threads read
-        }
-        __syncthreads();
-        found = sh[batch];
+    // full chunks: floor(L_b / c) per sequence
+    const int nfull = scan_find([&](int b) { return len_of(b) / chunk; }, k);
+    int b, p;
+    if (k < nfull) {
+        b = sh[NWV];
+        p = sh[NWV + 1];
     } else {
-        const int ntail = scan_find([&](int b) { return len_of(b) % chunk ? 1 : 0; }, i);
-        found = i < ntail ? sh[NWV] : -1;
+        // the (k - nfull)-th last chunk in order of decreasing length
+        const int i = k - nfull;
+        if (sorted) {
+            for (int c = tid; c < batch; c += NT) key[c] = len_of(c) % chunk;
+            __syncthreads();
+            for (int b = tid; b < batch; b += NT) {
+                const int kb = key[b];
+                int rank = 0;
+                for (int c = 0; c < batch; ++c) {
+                    const int kc = key[c];
+                    rank += (kc > kb) || (kc == kb && c < b);
+                }
+                perm[rank] = b;
+            }
+            __syncthreads();
+        }
+        scan_find([&](int r) { return len_of(sorted ? perm[r] : r) % chunk ? 1 : 0; }, i);
+        b = sorted ? perm[sh[NWV]] : sh[NWV];
+        p = len_of(b) / chunk;
     }
-    if (found < 0) return false;   // past the last item
-    b_out = found;
-    p_out = len_of(found) / chunk;
+    b_out = b;
+    p_out = p;
+    t0_out = p * chunk;
+    t1_out = min(t0_out + chunk, len_of(b));
     return true;
 }
 

@@ -247,7 +247,7 @@ template <int NS>
 __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
     const unsigned char* __restrict__ qrec, const u16* __restrict__ w_uv, const u16* __restrict__ cache,
     int64_t bstride, const int32_t* __restrict__ ctx_lens, int max_ctx, int h_q, int g, int s_q, int chunk,
-    int n_split, int nz, int batch, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_lse,
+    int n_split, int nz, int cap, int batch, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_lse,
     u16* __restrict__ out, float* __restrict__ lse_out) {
     constexpr int R = 16 * NS;                     // query rows of a workgroup
     static_assert(NS >= 1 && NS <= 4, "1..4 score waves");
@@ -274,15 +274,15 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
     // One chunk per sequence: item k is sequence k.  Several: the items are ordered
     // longest first (chunk_of_item), so the short last chunks of a ragged batch fill in
     // at the end.
-    int b = pair, p = 0;
+    int b = pair, p = 0, t0 = 0, t1 = 0;
     if (n_split > 1) {
-        if (!chunk_of_item<(NS + NV) * 64>(pair, ctx_lens, batch, max_ctx, chunk,
-                                           reinterpret_cast<int*>(lds.tiles[0]), b, p))
+        if (!chunk_of_item<(NS + NV) * 64>(pair, ctx_lens, batch, max_ctx, chunk, cap,
+                                           reinterpret_cast<int*>(lds.tiles[0]), b, p, t0, t1))
             return;
         __syncthreads();   // the item is known to every thread before the tiles reuse LDS
     }
     const int L = clampi(ctx_lens[b], 0, max_ctx);
-    const int t0 = p * chunk;
+    if (n_split == 1) t1 = min(chunk, L);
     const int RQ = s_q * h_q;
     const int na = min(NS, (RQ - z * R) / 16);     // active row tiles of the block (RQ % 16 == 0)
     const int tid = threadIdx.x;
@@ -305,7 +305,6 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
         }
         return;
     }
-    const int t1 = min(t0 + chunk, L);
     const int ntiles = (t1 - t0 + TT - 1) / TT;
     // tokens below t_full are visible to every query row and inside the chunk
     const int t_full = min(t1, clampi(L - s_q + 1, 0, L));
@@ -687,9 +686,12 @@ template <int NS>
 hipError_t launch_absorb_t(const DecodeArgs& a, int nz, hipStream_t st) {
     const int pairs = a.n_split * a.batch;
     dim3 grid(((pairs + 7) / 8) * 8 * nz);
+    // work items that run at once
+    static const int per_cu = blocks_per_cu(absorb_decode_kernel<NS>, (NS + NV) * 64);
+    const int cap = per_cu * a.cus / nz;
     hipLaunchKernelGGL((absorb_decode_kernel<NS>), grid, dim3((NS + NV) * 64), 0, st,
                        (const unsigned char*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride,
-                       a.ctx_lens, a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.n_split, nz, a.batch,
+                       a.ctx_lens, a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.n_split, nz, cap, a.batch,
                        a.scale * kLog2e, a.part_o, a.part_lse, (u16*)a.out, a.lse);
     return hipGetLastError();
 }

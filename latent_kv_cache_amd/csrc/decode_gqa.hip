@@ -35,6 +35,7 @@ constexpr int DH = 128;   // per-group key/value width
 constexpr int DR = 64;    // rotary key width
 constexpr int RK = 512;   // latent width
 constexpr int TT = 32;    // tokens per tile
+static_assert(kChunkAlign == kBf16TokenTile && kChunkAlign % TT == 0, "chunks are whole tiles");
 
 // Token held by k-slot e (0..7) of lane group q (0..3) in the P / V^T operands:
 // the softmax keeps S for tokens 16*(e/4) + 4q + (e%4), the D-layout of the two
@@ -136,12 +137,10 @@ __device__ __forceinline__ void store_tile(u16* lds, const u32x4 (&reg)[NLOAD], 
 
 // ---------------------------------------------------------------------------
 // GQA decode.  One-dimensional XCD-aware grid; block = NW waves.  Block id i runs on
-// XCD i % 8; its slot i / 8 gives the pair block z = slot % nz and the (sequence,
-// chunk) unit u = (slot / nz) * 8 + i % 8 = p * batch + bb, sequence b = (bb + p) mod
-// batch.  So the nz blocks that read the same tiles are 8 ids apart (one XCD,
-// dispatched together: the second read is an L2 hit), and chunk p of sequence b runs
-// on XCD (b + p) % 8, which spreads ragged batches evenly (chunk-major numbering would
-// put every sequence's first, always full, chunk on the same XCD).
+// XCD i % 8; its slot i / 8 gives the pair block z = slot % nz and the work item
+// u = (slot / nz) * 8 + i % 8, which chunk_of_item maps to a (sequence, chunk).  So the
+// nz blocks that read the same tiles are 8 ids apart (one XCD, dispatched together:
+// the second read is an L2 hit), and consecutive items run on consecutive XCDs.
 // The (group, 16-row tile) pairs of a sequence are numbered pair = j*RT + rt with
 // RT = ceil(rows_per_group / 16).  A wave owns RPW consecutive row tiles of one group
 // (RPW divides RT): its K_j and V_j operand reads from LDS then feed RPW MFMAs each,
@@ -150,11 +149,11 @@ __device__ __forceinline__ void store_tile(u16* lds, const u32x4 (&reg)[NLOAD], 
 // Block z handles waves units [z*NW, z*NW + NW) of the G * RT / RPW.
 // Rows of group j are numbered rho = s*hpg + hh (query token s, head j*hpg + hh).
 // ---------------------------------------------------------------------------
-template <int G, int NW, int RPW>
+template <int G, int NW, int RPW, int AHEAD>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
     const u16* __restrict__ q_nope, const u16* __restrict__ q_rope,
     const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
-    int max_ctx, int h_q, int s_q, int chunk, int n_split, int nz, int batch, float scale_log2,
+    int max_ctx, int h_q, int s_q, int chunk, int n_split, int nz, int cap, int batch, float scale_log2,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
     constexpr int W = 2 * G * DH + DR;
     constexpr int STRIDE = W + 16;   // row stride = 8 x odd dwords mod 64 banks
@@ -166,12 +165,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
     const int zb = slot % nz;
     const int unit = (slot / nz) * 8 + xcd;
     if (unit >= n_split * batch) return;      // padding of the last group of 8
-    int b, p;
-    if (!chunk_of_item<NT>(unit, ctx_lens, batch, max_ctx, chunk, reinterpret_cast<int*>(lds), b, p)) return;
+    int b, p, t0, t1;
+    if (!chunk_of_item<NT>(unit, ctx_lens, batch, max_ctx, chunk, cap, reinterpret_cast<int*>(lds), b, p, t0, t1)) return;
     const int L = clampi(ctx_lens[b], 0, max_ctx);
-    const int t0 = p * chunk;
     __syncthreads();                          // the item is known to every thread before the tile reuses LDS
-    const int t1 = min(t0 + chunk, L);
     const int ntiles = (t1 - t0 + TT - 1) / TT;
 
     const int tid = threadIdx.x;
@@ -196,6 +193,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
         qrow[rg] = (b * s_q + s) * h_q + h;
     }
 
+    // the first tile's loads go out before the queries', so the two round trips to memory
+    // overlap at the start of every item
+    const u16* seq = cache + (size_t)b * bstride;
+    u32x4 reg[AHEAD][NLOAD];
+#pragma unroll
+    for (int a = 0; a < AHEAD; ++a)
+        if (a == 0 || a < ntiles) load_tile<W, NT, NLOAD>(reg[a], seq + (size_t)(t0 + a * TT) * W, min(TT, t1 - t0 - a * TT), tid);
     // queries as the B operand of S^T = K Q^T: k-steps 0..3 over q^N, 4..5 over q^R
     f16x8 qv[RPW][6];
 #pragma unroll
@@ -220,20 +224,17 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
 #pragma unroll
     for (int rg = 0; rg < RPW; ++rg) st[rg] = SoftmaxState{kNegInf, 0.f};
 
-    const u16* seq = cache + (size_t)b * bstride;
-    u32x4 reg[NLOAD];
-    load_tile<W, NT, NLOAD>(reg, seq + (size_t)t0 * W, min(TT, t1 - t0), tid);
-
-    for (int it = 0; it < ntiles; ++it) {
+    // Tile it leaves staging buffer it % AHEAD for LDS, and the buffer takes tile it + AHEAD.
+    auto tile_step = [&](int it, u32x4 (&rb)[NLOAD]) {
         const int tb = t0 + it * TT;
         if (it > 0) __syncthreads();
-        store_tile<W, STRIDE, NT, NLOAD>(lds, reg, tid);
+        store_tile<W, STRIDE, NT, NLOAD>(lds, rb, tid);
         __syncthreads();
-        if (it + 1 < ntiles) {
-            const int tn = tb + TT;
-            load_tile<W, NT, NLOAD>(reg, seq + (size_t)tn * W, min(TT, t1 - tn), tid);
+        if (it + AHEAD < ntiles) {
+            const int tn = tb + AHEAD * TT;
+            load_tile<W, NT, NLOAD>(rb, seq + (size_t)tn * W, min(TT, t1 - tn), tid);
         }
-        if (!active) continue;
+        if (!active) return;
 
         f16x8 pb[RPW];
         {
@@ -279,6 +280,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
 #pragma unroll
             for (int rg = 0; rg < RPW; ++rg) oacc[rg][n] = mfma16h(a, pb[rg], oacc[rg][n]);
         }
+    };
+    // unrolled by AHEAD so that every staging buffer is addressed statically
+    for (int it = 0; it < ntiles; it += AHEAD) {
+#pragma unroll
+        for (int a = 0; a < AHEAD; ++a)
+            if (a == 0 || it + a < ntiles) tile_step(it + a, reg[a]);
     }
 
 #pragma unroll
@@ -332,7 +339,7 @@ template <int G, int NW, int RPW>
 __global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
     const u16* __restrict__ q_nope, const u16* __restrict__ q_rope,
     const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
-    int max_ctx, int h_q, int s_q, int chunk, int n_split, int nz, int batch, float scale_log2,
+    int max_ctx, int h_q, int s_q, int chunk, int n_split, int nz, int cap, int batch, float scale_log2,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
     constexpr int T16 = 16;
     constexpr int W = 2 * G * DH + DR;
@@ -345,12 +352,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
     const int zb = slot % nz;
     const int unit = (slot / nz) * 8 + xcd;
     if (unit >= n_split * batch) return;
-    int b, p;
-    if (!chunk_of_item<NT>(unit, ctx_lens, batch, max_ctx, chunk, reinterpret_cast<int*>(lds), b, p)) return;
+    int b, p, t0, t1;
+    if (!chunk_of_item<NT>(unit, ctx_lens, batch, max_ctx, chunk, cap, reinterpret_cast<int*>(lds), b, p, t0, t1)) return;
     const int L = clampi(ctx_lens[b], 0, max_ctx);
-    const int t0 = p * chunk;
     __syncthreads();
-    const int t1 = min(t0 + chunk, L);
     const int ntiles = (t1 - t0 + T16 - 1) / T16;
 
     const int tid = threadIdx.x;
@@ -375,6 +380,11 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
         qrow[rg] = (b * s_q + s) * h_q + h;
     }
 
+    // the first tile's loads go out before the queries', so the two round trips to memory
+    // overlap at the start of every item
+    const u16* seq = cache + (size_t)b * bstride;
+    u32x4 reg[NLOAD];
+    load_tile<W, NT, NLOAD, T16>(reg, seq + (size_t)t0 * W, min(T16, t1 - t0), tid);
     f16x8 qv[RPW][6];
 #pragma unroll
     for (int rg = 0; rg < RPW; ++rg)
@@ -397,10 +407,6 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
     SoftmaxState st[RPW];
 #pragma unroll
     for (int rg = 0; rg < RPW; ++rg) st[rg] = SoftmaxState{kNegInf, 0.f};
-
-    const u16* seq = cache + (size_t)b * bstride;
-    u32x4 reg[NLOAD];
-    load_tile<W, NT, NLOAD, T16>(reg, seq + (size_t)t0 * W, min(T16, t1 - t0), tid);
 
     for (int it = 0; it < ntiles; ++it) {
         const int tb = t0 + it * T16;
@@ -472,30 +478,36 @@ hipError_t launch_gqa16_t(const DecodeArgs& a, hipStream_t st) {
     const int waves = G * ((rows_g + 15) / 16) / RPW;
     const int nz = (waves + NW - 1) / NW;
     const int units = a.n_split * a.batch;
+    // work items that run at once
+    static const int per_cu = blocks_per_cu(gqa_decode16_kernel<G, NW, RPW>, NW * 64);
+    const int cap = per_cu * a.cus / nz;
     dim3 grid(((units + 7) / 8) * 8 * nz);
     hipError_t e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gqa_decode16_kernel<G, NW, RPW>), grid, dim3(NW * 64), 0, st,
                        (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.cache, a.bstride,
-                       a.ctx_lens, a.max_ctx, a.h_q, a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e,
+                       a.ctx_lens, a.max_ctx, a.h_q, a.s_q, a.chunk, a.n_split, nz, cap, a.batch, a.scale * kLog2e,
                        a.part_o, a.part_lse);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return record_if(a.ev_after, st);
 }
 
-template <int G, int NW, int RPW>
+template <int G, int NW, int RPW, int AHEAD>
 hipError_t launch_gqa_t(const DecodeArgs& a, hipStream_t st) {
     const int rows_g = a.s_q * (a.h_q / a.g);
     const int waves = G * ((rows_g + 15) / 16) / RPW;
     const int nz = (waves + NW - 1) / NW;
     const int units = a.n_split * a.batch;
+    // work items that run at once
+    static const int per_cu = blocks_per_cu(gqa_decode_kernel<G, NW, RPW, AHEAD>, NW * 64);
+    const int cap = per_cu * a.cus / nz;
     dim3 grid(((units + 7) / 8) * 8 * nz);
     hipError_t e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gqa_decode_kernel<G, NW, RPW>), grid, dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((gqa_decode_kernel<G, NW, RPW, AHEAD>), grid, dim3(NW * 64), 0, st,
                        (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.cache, a.bstride,
-                       a.ctx_lens, a.max_ctx, a.h_q, a.s_q, a.chunk, a.n_split, nz, a.batch, a.scale * kLog2e,
+                       a.ctx_lens, a.max_ctx, a.h_q, a.s_q, a.chunk, a.n_split, nz, cap, a.batch, a.scale * kLog2e,
                        a.part_o, a.part_lse);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -511,10 +523,10 @@ template <int G>
 hipError_t launch_gqa_g(const DecodeArgs& a, hipStream_t st) {
     const int rt = (a.s_q * (a.h_q / a.g) + 15) / 16;
     if (rt % 2 == 0 && G * rt > 8) {
-        if constexpr (G <= 4) return launch_gqa_t<G, 8, 2>(a, st);
+        if constexpr (G <= 4) return launch_gqa_t<G, 8, 2, 1>(a, st);
         else return launch_gqa16_t<G, 8, 2>(a, st);
     }
-    return launch_gqa_t<G, 8, 1>(a, st);
+    return launch_gqa_t<G, 8, 1, (G <= 4 ? 2 : 1)>(a, st);
 }
 
 }  // namespace

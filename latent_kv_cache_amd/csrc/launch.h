@@ -13,6 +13,7 @@ struct DecodeArgs {
     float scale;
     int batch, max_ctx;
     int n_split, chunk;                 // context chunks per sequence, tokens per chunk
+    int cus = 0;                        // compute units of the device
     const void* q_nope;
     const void* q_rope;
     const void* w_uk;                   // absorb only
@@ -30,6 +31,15 @@ struct DecodeArgs {
 };
 
 inline hipError_t record_if(hipEvent_t ev, hipStream_t st) { return ev ? hipEventRecord(ev, st) : hipSuccess; }
+
+// Blocks of `kernel` (launched with `threads` threads and no dynamic LDS) resident on
+// one compute unit at once; 1 if the runtime cannot tell.
+template <typename K>
+int blocks_per_cu(K kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
+    return n;
+}
 
 struct ExpandArgs {
     int h_q, g, r_kv, d_r, d_h;

@@ -142,11 +142,14 @@ def test_edge_lengths(gqla, s_q):
     both_paths(cfg, lens, gqla, 3, max_ctx=96, what=f"edges s_q{s_q}")
 
 
-@pytest.mark.parametrize("batch,seed", [(12, 0), (1040, 1)])
+@pytest.mark.parametrize("batch,seed", [(12, 0), (300, 2), (1040, 1)])
 def test_item_order(gqla, batch, seed):
-    """The GQA grid lists every full chunk first and then the sequences' shorter last
-    chunks, longest first (in sequence order above 1024 sequences).  Lengths mix full
-    chunks, tails of equal length, single rows and empty sequences."""
+    """Both split-K item layouts.  12 sequences in 3 splits make at most 36 items, which
+    run at once: every sequence is cut into chunks of equal size (rounded up to 32
+    rows), so chunk boundaries fall off the uniform grid.  300 and 1040 sequences make
+    more items than the device runs at once: full chunks first, then the shorter last
+    chunks, longest first (300 sequences) or in sequence order (1040).  Lengths mix
+    full chunks, tails of equal length, single rows and empty sequences."""
     cfg = synth.config(2).with_(batch=batch)
     rng = np.random.default_rng(7 + seed)
     if batch <= 16:
@@ -159,11 +162,14 @@ def test_item_order(gqla, batch, seed):
     both_paths(cfg, lens, gqla, splits, max_ctx=max_ctx, what=f"order B{batch}")
 
 
-def test_chunk_boundary_causal(gqla):
-    """s_q = 2 with L - 1 on a chunk boundary: query 0 sees nothing of the last chunk."""
+@pytest.mark.parametrize("lens,max_ctx", [([97, 65], 129), ([33, 20], 64)])
+def test_chunk_boundary_causal(gqla, lens, max_ctx):
+    """s_q = 2 with a chunk boundary near row L - 1, which only query 1 sees.  In 2
+    splits max_ctx 129 gives chunks of at most 96 rows, cut evenly into 64 + 33 at
+    L = 97; max_ctx 64 gives chunks of 32, and L = 33 puts row L - 1 alone in chunk 1
+    (query 0 sees nothing there)."""
     cfg = synth.config(4, s_q=2).with_(batch=2)
-    # max_ctx 129 in 2 splits -> chunks of 96; L = 97 puts row L - 1 alone in chunk 1
-    both_paths(cfg, [97, 65], gqla, 2, max_ctx=129, what="causal-boundary")
+    both_paths(cfg, lens, gqla, 2, max_ctx=max_ctx, what=f"causal-boundary {lens}")
 
 
 @pytest.mark.parametrize("s_q", [1, 2])
