@@ -1,7 +1,7 @@
 """Summarise a rocprofv3 kernel-trace database (rocpd SQLite) as a markdown table.
 
 Usage: python bench_profile.py <results.db> [--command "..."]
-Per kernel name: dispatch count, average / min / max duration (us), total (us),
+Per kernel name: dispatch count, median / average / min / max duration (us), total (us),
 grid and workgroup sizes, VGPR/AGPR counts and LDS bytes per workgroup.
 """
 from __future__ import annotations
@@ -19,7 +19,11 @@ def summarise(db_path: str):
                   max(grid_x), max(grid_y), max(grid_z), max(workgroup_x),
                   max(vgpr_count), max(accum_vgpr_count), max(lds_size)
            from kernels group by name order by sum(end - start) desc""").fetchall()
-    return rows
+    durs = {}
+    for name, d in db.execute("select name, end - start from kernels"):
+        durs.setdefault(name, []).append(d / 1000.0)
+    med = {n: sorted(v)[len(v) // 2] for n, v in durs.items()}
+    return [(r[0], r[1], med[r[0]]) + tuple(r[2:]) for r in rows]
 
 
 def short(name: str) -> str:
@@ -35,11 +39,11 @@ def main(argv=None) -> int:
     rows = summarise(a.db)
     if a.command:
         print(f"Command: `{a.command}`\n")
-    print("| kernel | n | avg us | min us | max us | total us | grid | wg | vgpr | agpr | lds B |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    print("| kernel | n | median us | avg us | min us | max us | total us | grid | wg | vgpr | agpr | lds B |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in rows:
-        print(f"| {short(r[0])} | {r[1]} | {r[2]:.2f} | {r[3]:.2f} | {r[4]:.2f} | {r[5]:.1f} | "
-              f"{r[6]}x{r[7]}x{r[8]} | {r[9]} | {r[10]} | {r[11]} | {r[12]} |")
+        print(f"| {short(r[0])} | {r[1]} | {r[2]:.2f} | {r[3]:.2f} | {r[4]:.2f} | {r[5]:.2f} | {r[6]:.1f} | "
+              f"{r[7]}x{r[8]}x{r[9]} | {r[10]} | {r[11]} | {r[12]} | {r[13]} |")
     return 0
 
 
