@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgqla.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "decode_gqa.hip", "decode_absorb.hip", "expand_bf16.hip", "f32_path.hip", "combine.hip", "append.hip", "probe.hip", "decode_sparse.hip"]
+SOURCES = ["api.hip", "decode_gqa.hip", "decode_absorb.hip", "expand_bf16.hip", "f32_path.hip", "f32_mfma.hip", "combine.hip", "append.hip", "probe.hip", "decode_sparse.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-mcode-object-version=5",

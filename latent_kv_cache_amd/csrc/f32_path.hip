@@ -3,9 +3,11 @@
 // Method: "GQLA: Group-Query Latent Attention for Hardware-Adaptive LLM
 // Decoding", technical summary section 2 (Architecture).  Same arithmetic as
 // the bf16 MFMA kernels, written for fp32 storage and shapes that are not
-// multiples of the MFMA tiles: one workgroup per (context chunk, sequence,
-// query row), scores of the chunk in LDS, two-pass softmax within the chunk,
-// and the chunk's normalised output plus log-sum-exp as the split-K partial.
+// multiples of the MFMA tiles (the decode launchers below take the fp32 MFMA
+// kernels of f32_mfma.hip whenever the shape fits them): one workgroup per
+// (context chunk, sequence, query row), scores of the chunk in LDS, two-pass
+// softmax within the chunk, and the chunk's normalised output plus log-sum-exp
+// as the split-K partial.
 #include "common.h"
 #include "launch.h"
 
@@ -188,6 +190,7 @@ __global__ __launch_bounds__(NT) void expand_f32_kernel(
 }  // namespace
 
 hipError_t launch_absorb_f32(const DecodeArgs& a, hipStream_t st) {
+    if (absorb_f32_mfma_fits(a)) return launch_absorb_f32_mfma(a, st);
     dim3 grid(a.n_split, a.batch, a.s_q * a.h_q);
     hipError_t e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;
@@ -201,6 +204,7 @@ hipError_t launch_absorb_f32(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t st) {
+    if (gqa_f32_mfma_fits(a)) return launch_gqa_f32_mfma(a, st);
     dim3 grid(a.n_split, a.batch, a.s_q * a.h_q);
     hipError_t e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;

@@ -88,6 +88,11 @@ hipError_t launch_gqa_sparse(const DecodeArgs& a, const int32_t* indices, int to
 // fp32 vector path (generic dims within the documented bounds)
 hipError_t launch_absorb_f32(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t st);
+// fp32 MFMA kernels, for shapes of whole MFMA tiles (launch_*_f32 pick them when they fit)
+bool absorb_f32_mfma_fits(const DecodeArgs& a);
+bool gqa_f32_mfma_fits(const DecodeArgs& a);
+hipError_t launch_absorb_f32_mfma(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_gqa_f32_mfma(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_expand_f32(const ExpandArgs& a, hipStream_t st);
 
 // device peak probes (block the host until done)

@@ -75,7 +75,10 @@ def test_tiny_fp32_ragged_multi(gqla):
 @pytest.mark.parametrize("d_h", [48, 256])
 def test_fp32_head_widths(gqla, d_h):
     """d_h = 48 and 256: the combine's one- and four-outputs-per-lane layouts (upper lanes
-    idle at 48), with three chunks per sequence so every row is merged."""
+    idle at 48), with three chunks per sequence so every row is merged.  d_h = 48 is not a
+    whole MFMA tile (vector-ALU kernels on both paths); at 256 the absorb path runs the
+    MFMA kernel and the GQA path, whose staged queries would pass the MFMA kernel's
+    64 KB of LDS, the vector-ALU one."""
     cfg = synth.config(1).with_(batch=2, d_h=d_h)
     both_paths(cfg, [256, 77], gqla, 3, max_ctx=256, what=f"tiny d_h={d_h}")
 
@@ -101,6 +104,14 @@ def test_flagship_heads_few_groups(gqla, g):
     both_paths(cfg, [1500, 77], gqla, 0, max_ctx=1536, what=f"g={g}")
     # the chain against the textbook at the long sequence, where the stored rows' rounding averages out
     both_paths(cfg, [1500, 77], gqla, 0, seqs=[0], max_ctx=1536, what=f"g={g} e2e", end_to_end=True)
+
+
+@pytest.mark.parametrize("h_q,s_q", [(16, 4), (32, 3)])
+def test_fp32_row_tiles(gqla, h_q, s_q):
+    """fp32 at g = 1, h_q s_q query rows per group: the MFMA kernels' four 16-row waves at
+    64 rows, and past their 64 rows (96) the vector-ALU kernels."""
+    cfg = synth.config(1, g=1, s_q=s_q).with_(batch=2, h_q=h_q)
+    both_paths(cfg, [256, 45], gqla, 3, max_ctx=256, what=f"fp32 rows h_q={h_q} s_q={s_q}")
 
 
 @pytest.mark.parametrize("g", [1, 16])
