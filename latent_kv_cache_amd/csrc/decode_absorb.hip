@@ -38,12 +38,14 @@ constexpr int QREC = 2176;
 constexpr int QHI = 0, QLO = 1024, QROPE = 2048;
 
 // ---------------------------------------------------------------------------
-// Prologue: one block per (64 rows of group j, j); 4 waves of 16 rows.  Rows of group j
-// are numbered iota = (b*s_q + s)*hpg + hh.  The contraction runs over d, strided in the
-// [g][d_h][r_kv] layout, so each quarter of W_UK[j]'s columns (128 d x 128 r, 36 KB with
-// the pad) is staged row-major in LDS and the A operand (W_UK^T) is formed with
-// transposing LDS reads: 4 rows d x 16 columns r per 16-lane group.  A lane ends with
-// the 128 columns 16 mt + 4 q4 + i (mt = 0..31, i = 0..3) of its row r16.
+// Prologue: one block per (64 rows of group j, j, quarter qc of the latent columns); 4
+// waves of 16 rows.  Rows of group j are numbered iota = (b*s_q + s)*hpg + hh.  The
+// contraction runs over d, strided in the [g][d_h][r_kv] layout, so the block stages its
+// quarter of W_UK[j]'s columns (128 d x 128 r, 36 KB with the pad) row-major in LDS and
+// forms the A operand (W_UK^T) with transposing LDS reads: 4 rows d x 16 columns r per
+// 16-lane group.  A lane ends with the 32 columns 128 qc + 16 mt + 4 q4 + i (mt = 0..7,
+// i = 0..3) of its row r16.  Four blocks per row block keep even small batches on more
+// compute units than one block per row block would (one per 64 rows and group).
 // ---------------------------------------------------------------------------
 constexpr int PRO_COLS = RK / 4;
 constexpr int PRO_STRIDE = PRO_COLS + 16;
@@ -52,10 +54,28 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
     const u16* __restrict__ q_nope, const u16* __restrict__ q_rope, const u16* __restrict__ w_uk,
     unsigned char* __restrict__ qrec, int batch, int h_q, int g, int s_q, float scale_log2) {
     __shared__ __attribute__((aligned(16))) u16 wt[DH * PRO_STRIDE];
-    const int j = blockIdx.y;
+    const int j = blockIdx.y, qc = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int q4 = lane >> 4, r16 = lane & 15;
+
+    // stage columns 128 qc .. 128 qc + 127 of W_UK[j]: 2048 chunks of 16 bytes, 8 per
+    // thread, all eight loads in flight before the first store
+    constexpr int CPRW = PRO_COLS / 8;   // 16-byte chunks per staged row
+    {
+        const u16* wj = w_uk + (size_t)j * DH * RK + qc * PRO_COLS;
+        u32x4 v[DH * CPRW / 256];
+#pragma unroll
+        for (int k = 0; k < DH * CPRW / 256; ++k) {
+            const int c = k * 256 + tid;
+            v[k] = *reinterpret_cast<const u32x4*>(wj + (size_t)(c / CPRW) * RK + (c % CPRW) * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < DH * CPRW / 256; ++k) {
+            const int c = k * 256 + tid;
+            *reinterpret_cast<u32x4*>(wt + (c / CPRW) * PRO_STRIDE + (c % CPRW) * 8) = v[k];
+        }
+    }
 
     const int hpg = h_q / g;
     const int nrows = batch * s_q * hpg;
@@ -82,64 +102,48 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
             qb[kd] = zero_bf16x8();
         }
     }
+    __syncthreads();
 
-    floatx4 acc[RK / 16];
+    floatx4 acc[PRO_COLS / 16];
     const u16* abase = wt + (4 * q4 + (r16 >> 2)) * PRO_STRIDE + 4 * (r16 & 3);
-    constexpr int CPRW = PRO_COLS / 8;   // 16-byte chunks per staged row
 #pragma unroll
-    for (int qc = 0; qc < 4; ++qc) {
-        // stage columns 128 qc .. 128 qc + 127 of W_UK[j]: 2048 chunks of 16 bytes, 8 per
-        // thread, all eight loads in flight before the first store
-        const u16* wj = w_uk + (size_t)j * DH * RK + qc * PRO_COLS;
-        u32x4 v[DH * CPRW / 256];
+    for (int mt = 0; mt < PRO_COLS / 16; ++mt) {
+        floatx4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < DH * CPRW / 256; ++k) {
-            const int c = k * 256 + tid;
-            v[k] = *reinterpret_cast<const u32x4*>(wj + (size_t)(c / CPRW) * RK + (c % CPRW) * 8);
+        for (int kd = 0; kd < DH / 32; ++kd) {
+            const u16* pa = abase + kd * 32 * PRO_STRIDE + mt * 16;
+            const u32x2 lo = lds_read_tr16(pa);
+            const u32x2 hi = lds_read_tr16(pa + 16 * PRO_STRIDE);
+            a = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), qb[kd], a);
         }
-        if (qc > 0) __syncthreads();   // the previous quarter's reads are done
-#pragma unroll
-        for (int k = 0; k < DH * CPRW / 256; ++k) {
-            const int c = k * 256 + tid;
-            *reinterpret_cast<u32x4*>(wt + (c / CPRW) * PRO_STRIDE + (c % CPRW) * 8) = v[k];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int mt = 0; mt < PRO_COLS / 16; ++mt) {
-            floatx4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kd = 0; kd < DH / 32; ++kd) {
-                const u16* pa = abase + kd * 32 * PRO_STRIDE + mt * 16;
-                const u32x2 lo = lds_read_tr16(pa);
-                const u32x2 hi = lds_read_tr16(pa + 16 * PRO_STRIDE);
-                a = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), qb[kd], a);
-            }
-            acc[qc * (PRO_COLS / 16) + mt] = a;
-        }
+        acc[mt] = a;
     }
 
     if (!ok) return;
     // x = q~ * scale * log2(e) (fp32) as hi = bf16(x) and lo = bf16(x - hi)
 #pragma unroll
-    for (int c = 0; c < RK / 16; ++c) {
-        // columns 16 c + 4 q4 + i of the natural latent order (c = 8 qc + mt)
-        const int col = 16 * c + 4 * q4;
+    for (int mt = 0; mt < PRO_COLS / 16; ++mt) {
+        // columns 128 qc + 16 mt + 4 q4 + i of the natural latent order
+        const int col = qc * PRO_COLS + 16 * mt + 4 * q4;
         u16 hs[4], ls[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float x = acc[c][i] * scale_log2;
+            const float x = acc[mt][i] * scale_log2;
             hs[i] = f2bf(x);
             ls[i] = f2bf(x - bf2f(hs[i]));
         }
         *reinterpret_cast<u32x2*>(dst + QHI + col * 2) = u32x2{pack2(hs[0], hs[1]), pack2(hs[2], hs[3])};
         *reinterpret_cast<u32x2*>(dst + QLO + col * 2) = u32x2{pack2(ls[0], ls[1]), pack2(ls[2], ls[3])};
     }
-    // q^R: 64 elements; lane group q4 copies elements 16 q4 .. 16 q4 + 15
+    // q^R: 64 elements, copied by the first quarter's block; lane group q4 copies
+    // elements 16 q4 .. 16 q4 + 15
+    if (qc == 0) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int off = q4 * 16 + c * 8;
-        *reinterpret_cast<u32x4*>(dst + QROPE + off * 2) =
-            *reinterpret_cast<const u32x4*>(q_rope + qrow * DR + off);
+        for (int c = 0; c < 2; ++c) {
+            const int off = q4 * 16 + c * 8;
+            *reinterpret_cast<u32x4*>(dst + QROPE + off * 2) =
+                *reinterpret_cast<const u32x4*>(q_rope + qrow * DR + off);
+        }
     }
 }
 
@@ -705,7 +709,7 @@ size_t absorb_qrec_bytes() { return QREC; }
 hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st) {
     const int hpg = a.h_q / a.g;
     const int rows_per_group = a.batch * a.s_q * hpg;
-    dim3 pgrid((rows_per_group + 63) / 64, a.g);
+    dim3 pgrid((rows_per_group + 63) / 64, a.g, RK / PRO_COLS);
     hipLaunchKernelGGL(absorb_prologue_kernel, pgrid, dim3(256), 0, st,
                        (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.w_uk, (unsigned char*)a.qhat,
                        a.batch, a.h_q, a.g, a.s_q, a.scale * kLog2e);
