@@ -504,6 +504,19 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
         const int goff = (4 * q4 + (r16 >> 2)) * STRIDE + VCOLS * vw + 4 * (r16 & 3);
         // Step k >= 1 of the pipeline: U += C_{k-1}^T P_{k-1}, loads of tile k+2, wait for
         // this wave's loads of tile k+1.
+        // A operands of a step, all eight column tiles (transposing reads of bf16), read at
+        // the end of the step before: after the barrier only P and the rescale factors
+        // are left to read, and the barrier's burst of LDS requests is smaller
+        u32x4 ra[NCT];
+        auto read_a = [&](const u16* bt, int go) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const u16* p0 = bt + go + 16 * ct;
+                const u32x2 lo = lds_read_tr16(p0);
+                const u32x2 hi = lds_read_tr16(p0 + 16 * STRIDE);
+                ra[ct] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        };
         auto vstep = [&](int k) {
             opaque_offsets();
             // per-lane bases, opaque per step: the addresses derived from them are then
@@ -511,31 +524,23 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
             // loop for all four buffers and held in registers
             int go = goff, ln = lane;
             asm volatile("" : "+v"(go), "+v"(ln));
-            const u16* const bval = bufp(k + 3);       // tile k-1
             const u16* const pr = pbuf[(k + 1) & 1];
             const float* const ar = abuf[(k + 1) & 1];
             const bool more = k + 2 < ntiles;
             // the loads of tile k+2 go out first: they have until the end of step k+1 to land
             if (more) dma_tile(k + 2, lds_addr(bufp(k + 2)));
-            // All of the step's LDS reads are issued before the first wait: the rescale
-            // factors, P, and the A operands of all eight column tiles (transposing reads
-            // of bf16).  The A operands are then converted to fp16, and only after that do
-            // the MFMAs start: the conversion (VALU) runs beside the score wave's MFMAs on
-            // this SIMD, and this wave's MFMAs beside the score wave's softmax.
+            // The rescale factors and P are read (the A operands are already in flight
+            // from the step before); the A operands are then converted to fp16, and only
+            // after that do the MFMAs start: the conversion (VALU) runs beside the score
+            // wave's MFMAs on this SIMD, and this wave's MFMAs beside the score wave's
+            // softmax.
             float al[NS];
 #pragma unroll
             for (int rt = 0; rt < NS; ++rt) al[rt] = ar[16 * rt + (ln & 15)];
             f16x8 pv[NS];
 #pragma unroll
             for (int rt = 0; rt < NS; ++rt) pv[rt] = ld_f16x8(pr + (rt * 64 + ln) * 8);
-            u32x4 ra[NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const u16* p0 = bval + go + 16 * ct;
-                const u32x2 lo = lds_read_tr16(p0);
-                const u32x2 hi = lds_read_tr16(p0 + 16 * STRIDE);
-                ra[ct] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-            }
+
             // rescale rows whose reference rose at tile k-1 (rare)
             bool any = false;
 #pragma unroll
@@ -557,6 +562,7 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
                 for (int rt = 0; rt < NS; ++rt) uacc[ct][rt] = mfma16h(a, pv[rt], uacc[ct][rt]);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (k < ntiles) read_a(bufp(k), go);   // the next step's A operands: tile k, in LDS since step k-1
             wait_own(more);
             block_sync();
         };
@@ -573,6 +579,7 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
             wait_own(more);
             block_sync();
         }
+        read_a(bufp(0), goff);
 #pragma unroll 1
         for (int k = 1; k <= ntiles; ++k) vstep(k);
         // no direct load may still be writing this workgroup's LDS
