@@ -82,7 +82,8 @@ typedef struct gqla_shape {
 } gqla_shape;
 
 /* Bytes of device workspace a decode call needs (split-K partials, and for the
- * absorb path one absorbed-query record per query row).  num_splits: 0 = automatic, else an upper
+ * bf16 absorb path one absorbed-query record per query row and a copy of W_UV,
+ * g * d_h * r_kv elements, rewritten by every call in the order its kernel reads it).  num_splits: 0 = automatic, else an upper
  * bound on context chunks per sequence.  For GQLA_PATH_SPARSE the max_ctx argument
  * is the index-list length topk (the chunks split the list).  Returns GQLA_OK and
  * writes *bytes. */

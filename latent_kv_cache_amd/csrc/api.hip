@@ -195,7 +195,7 @@ double split_estimate(const int32_t* lens, int batch, int max_ctx, int chunk, in
 }
 
 struct Layout {
-    size_t part_o, part_lse, qhat, total;
+    size_t part_o, part_lse, qhat, wpack, total;
 };
 
 Layout layout(const gqla_shape& s, int path, int batch, const Plan& p) {
@@ -205,7 +205,11 @@ Layout layout(const gqla_shape& s, int path, int batch, const Plan& p) {
     l.part_lse = align256(l.part_o + (size_t)p.n_split * rows * s.d_h * sizeof(float));
     l.qhat = align256(l.part_lse + (size_t)p.n_split * rows * sizeof(float));
     size_t end = l.qhat;
-    if (path == GQLA_PATH_ABSORB && s.dtype == GQLA_BF16) end = align256(l.qhat + rows * gqla::absorb_qrec_bytes());
+    l.wpack = l.qhat;
+    if (path == GQLA_PATH_ABSORB && s.dtype == GQLA_BF16) {
+        l.wpack = align256(l.qhat + rows * gqla::absorb_qrec_bytes());
+        end = align256(l.wpack + gqla::absorb_wpack_bytes(s.g));
+    }
     l.total = end;
     return l;
 }
@@ -324,6 +328,7 @@ gqla_status decode_common(int path, const gqla_shape* sp, int32_t batch, int32_t
     a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
     a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
     a.qhat = ws + lay.qhat;
+    a.wpack = ws + lay.wpack;
     a.ev_before = g_ev_before;
     a.ev_after = g_ev_after;
 
@@ -565,6 +570,7 @@ gqla_status gqla_decode_gqa_sparse(const gqla_shape* shape, int32_t batch, int32
     a.part_o = reinterpret_cast<float*>(ws + lay.part_o);
     a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
     a.qhat = nullptr;
+    a.wpack = nullptr;
     a.ev_before = g_ev_before;
     a.ev_after = g_ev_after;
     a.n_merge = p.n_split;

@@ -50,12 +50,36 @@ constexpr int QHI = 0, QLO = 1024, QROPE = 2048;
 constexpr int PRO_COLS = RK / 4;
 constexpr int PRO_STRIDE = PRO_COLS + 16;
 
+// W_UV in the order the attention kernel's epilogue reads it: for group j, 128-column
+// block cb, 16-row tile dt and k-step ks, the 64 lanes' 16-byte A operands (lane (q, r16):
+// row 16 dt + r16, columns 128 cb + 32 ks + 8 q .. + 7) lie side by side, so one wave
+// instruction loads 1 KB of contiguous memory (the rows of W_UV itself give 64 bytes per
+// row and 16 rows per instruction, at well under half the rate).  Element offset (u16).
+__device__ __forceinline__ size_t wpack_index(int j, int cb, int dt, int ks, int lane) {
+    return ((((size_t)j * 4 + cb) * (DH / 16) + dt) * 4 + ks) * 512 + (size_t)lane * 8;
+}
+
 __global__ __launch_bounds__(256) void absorb_prologue_kernel(
     const u16* __restrict__ q_nope, const u16* __restrict__ q_rope, const u16* __restrict__ w_uk,
-    unsigned char* __restrict__ qrec, int batch, int h_q, int g, int s_q, float scale_log2) {
+    const u16* __restrict__ w_uv, unsigned char* __restrict__ qrec, u16* __restrict__ wpack, int batch, int h_q,
+    int g, int s_q, float scale_log2) {
     __shared__ __attribute__((aligned(16))) u16 wt[DH * PRO_STRIDE];
     const int j = blockIdx.y, qc = blockIdx.z;
     const int tid = threadIdx.x;
+    // W_UV[j], columns 128 qc .. 128 qc + 127, in the attention kernel's epilogue operand
+    // order (see wpack_index): eight 16-row tiles dt of 256 pieces of 16 bytes, one piece
+    // per thread.  The first min(8, row blocks) row blocks share the tiles out; the first
+    // tile of each is loaded beside the W_UK staging below.
+    const int nwb = min((int)gridDim.x, DH / 16);
+    const bool wrep = blockIdx.x < nwb;
+    const int wln = tid & 63, wks = tid >> 6;
+    auto wsrc = [&](int dt) {
+        return reinterpret_cast<const u32x4*>(w_uv + ((size_t)j * DH + 16 * dt + (wln & 15)) * RK + PRO_COLS * qc +
+                                              32 * wks + 8 * (wln >> 4));
+    };
+    auto wdst = [&](int dt) { return reinterpret_cast<u32x4*>(wpack + wpack_index(j, qc, dt, wks, wln)); };
+    u32x4 wv = {0u, 0u, 0u, 0u};
+    if (wrep) wv = *wsrc(blockIdx.x);
     const int lane = tid & 63, wave = tid >> 6;
     const int q4 = lane >> 4, r16 = lane & 15;
 
@@ -75,6 +99,11 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
             const int c = k * 256 + tid;
             *reinterpret_cast<u32x4*>(wt + (c / CPRW) * PRO_STRIDE + (c % CPRW) * 8) = v[k];
         }
+    }
+    if (wrep) {
+        *wdst(blockIdx.x) = wv;
+        // grids of fewer than eight row blocks: the remaining tiles
+        for (int dt = blockIdx.x + nwb; dt < DH / 16; dt += nwb) *wdst(dt) = *wsrc(dt);
     }
 
     const int hpg = h_q / g;
@@ -249,7 +278,7 @@ __device__ __forceinline__ f16x8 softmax_tile(SoftmaxState& st, const float (&sc
 
 template <int NS>
 __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
-    const unsigned char* __restrict__ qrec, const u16* __restrict__ w_uv, const u16* __restrict__ cache,
+    const unsigned char* __restrict__ qrec, const u16* __restrict__ wpack, const u16* __restrict__ cache,
     int64_t bstride, const int32_t* __restrict__ ctx_lens, int max_ctx, int h_q, int g, int s_q, int chunk,
     int n_split, int nz, int cap, int batch, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_lse,
     u16* __restrict__ out, float* __restrict__ lse_out) {
@@ -610,7 +639,8 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
         const float inv = l > 0.f ? 1.f / l : 0.f;
         // U^T as the B operand of o^T = W_UV[j] U^T: in k-step ks, k-slot e of lane group
         // q4 is latent column VCOLS cb + 32 ks + 8 q4 + e, so that each lane's weight
-        // operand is 16 contiguous bytes of a W_UV row.  Column 16 ct + 4 q + i of u sits
+        // operand is 16 contiguous bytes of a W_UV row (read from the packed copy the
+        // prologue wrote, where a wave's 64 operands are 1 KB in a row).  Column 16 ct + 4 q + i of u sits
         // in column tile ct, lane r16 + 16 q, element i of the stored accumulators, so
         // slots 0-3 come from lane group 2 (q4 & 1) and slots 4-7 from the next one, of
         // column tile 2 ks + q4 / 2.  u / l is carried as three bf16 terms (about 24
@@ -649,13 +679,12 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
         for (int jj = jlo; jj <= jhi; ++jj) {
             // all of the group's weight operands for these columns are loaded before the
             // first MFMA (one round trip to L2 per unit and group)
-            const u16* wrow = w_uv + (size_t)jj * DH * RK + VCOLS * cb + (size_t)r16 * RK + q4 * 8;
             u32x4 wa[DH / 16][NCT / 2];
 #pragma unroll
             for (int dt = 0; dt < DH / 16; ++dt)
 #pragma unroll
                 for (int ks = 0; ks < NCT / 2; ++ks)
-                    wa[dt][ks] = *reinterpret_cast<const u32x4*>(wrow + (size_t)dt * 16 * RK + ks * 32);
+                    wa[dt][ks] = *reinterpret_cast<const u32x4*>(wpack + wpack_index(jj, cb, dt, ks, lane));
 #pragma unroll
             for (int dt = 0; dt < DH / 16; ++dt) {
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -701,7 +730,7 @@ hipError_t launch_absorb_t(const DecodeArgs& a, int nz, hipStream_t st) {
     static const int per_cu = blocks_per_cu(absorb_decode_kernel<NS>, (NS + NV) * 64);
     const int cap = per_cu * a.cus / nz;
     hipLaunchKernelGGL((absorb_decode_kernel<NS>), grid, dim3((NS + NV) * 64), 0, st,
-                       (const unsigned char*)a.qhat, (const u16*)a.w_uv, (const u16*)a.cache, a.bstride,
+                       (const unsigned char*)a.qhat, (const u16*)a.wpack, (const u16*)a.cache, a.bstride,
                        a.ctx_lens, a.max_ctx, a.h_q, a.g, a.s_q, a.chunk, a.n_split, nz, cap, a.batch,
                        a.scale * kLog2e, a.part_o, a.part_lse, (u16*)a.out, a.lse);
     return hipGetLastError();
@@ -713,13 +742,15 @@ int absorb_block_rows(int query_rows) { return query_rows < 64 ? query_rows : 64
 
 size_t absorb_qrec_bytes() { return QREC; }
 
+size_t absorb_wpack_bytes(int g) { return (size_t)g * DH * RK * sizeof(u16); }
+
 hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st) {
     const int hpg = a.h_q / a.g;
     const int rows_per_group = a.batch * a.s_q * hpg;
     dim3 pgrid((rows_per_group + 63) / 64, a.g, RK / PRO_COLS);
     hipLaunchKernelGGL(absorb_prologue_kernel, pgrid, dim3(256), 0, st,
-                       (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.w_uk, (unsigned char*)a.qhat,
-                       a.batch, a.h_q, a.g, a.s_q, a.scale * kLog2e);
+                       (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.w_uk, (const u16*)a.w_uv,
+                       (unsigned char*)a.qhat, (u16*)a.wpack, a.batch, a.h_q, a.g, a.s_q, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int RQ = a.s_q * a.h_q;

@@ -26,6 +26,7 @@ struct DecodeArgs {
     float* part_o;                      // [n_split][batch][s_q][h_q][d_h]
     float* part_lse;                    // [n_split][batch][s_q][h_q]
     void* qhat;                         // absorb bf16: [batch][s_q*h_q] absorbed-query records
+    void* wpack;                        // absorb bf16: W_UV in the epilogue's operand order
     int n_merge = 0;                    // combine: 0 = the chunks covering L_b, else all n_merge chunks
     hipEvent_t ev_before, ev_after;     // optional, recorded around the main attention kernel
 };
@@ -81,6 +82,7 @@ hipError_t launch_expand_bf16(const ExpandArgs& a, hipStream_t st);
 bool gqa_bf16_supported(int g, int rows_per_group);
 int absorb_block_rows(int query_rows);     // query rows per absorb workgroup (16, 32, 48 or 64)
 size_t absorb_qrec_bytes();                // workspace bytes of one absorbed-query record
+size_t absorb_wpack_bytes(int g);          // workspace bytes of W_UV in the epilogue's operand order
 
 // sparse GQLA over per-(token, group) index lists (bf16 MFMA or fp32)
 hipError_t launch_gqa_sparse(const DecodeArgs& a, const int32_t* indices, int topk, bool bf16, hipStream_t st);
