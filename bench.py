@@ -355,14 +355,19 @@ def main(argv=None):
     rq = cfg.s_q * cfg.h_q
     absorb_name = "absorb_decode_kernel<%d>" % min(4, rq // 16)
     # the GQA launcher's choice: two row tiles per wave when a group has an even number
-    # of 16-row tiles and one per wave would need more than one workgroup (16-token
-    # tiles at g = 8)
+    # of 16-row tiles and one per wave would need more than one workgroup; tiles loaded
+    # straight into LDS (16 rows at g = 8, 32 below) except at g = 1 and, at g = 8 with
+    # one row tile per wave, for chunks longer than 1024 tokens
     rt = (cfg.s_q * (cfg.h_q // cfg.g) + 15) // 16
-    if rt % 2 == 0 and cfg.g * rt > 8:
-        gqa_name = ("gqa_decode_kernel<%d, 8, 2, 1>" % cfg.g) if cfg.g <= 4 else ("gqa_decode16_kernel<%d, 8, 2>" % cfg.g)
+    two = rt % 2 == 0 and cfg.g * rt > 8
+    rpw = 2 if two else 1
+    tr = 16 if cfg.g == 8 else 32
+    if cfg.g == 1:
+        gqa_name = "gqa_decode_kernel<1, 8, %d, %d>" % (rpw, 1 if two else 2)
+    elif cfg.g == 8 and not two and split_g[1] > 1024:
+        gqa_name = "gqa_decode_kernel<8, 8, 1, 1>"
     else:
-        # one row tile per wave; two tiles staged ahead at g <= 4
-        gqa_name = "gqa_decode_kernel<%d, 8, 1, %d>" % (cfg.g, 2 if cfg.g <= 4 else 1)
+        gqa_name = "gqa_dma_kernel<%d, 8, %d, %d>" % (cfg.g, rpw, tr)
     paths = {"absorb": path_rec(work_a, call_a, kern_a, split_a, absorb_name),
              "gqa": path_rec(work_g, call_g, kern_g, split_g, gqa_name)}
 

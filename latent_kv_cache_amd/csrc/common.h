@@ -257,6 +257,14 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t
                  : "memory", "m0");
 }
 
+// dma16 with the streaming hint (nt): for data that is read once.
+__device__ __forceinline__ void dma16_nt(const void* gbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
 }

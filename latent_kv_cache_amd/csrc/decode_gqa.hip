@@ -302,19 +302,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------
-// 16-token tiles, for g = 8 with two row tiles per wave (s_q = 2 at 16 heads per
-// group).  Half-height tiles halve the staging registers and the score accumulators,
-// which is what lets one wave hold two row tiles' queries, accumulators and softmax
-// state at g = 8 within 256 registers; one block then covers all 16 (group, row tile)
-// pairs and reads every tile from HBM once.  The scores use the 16x16x32 MFMA over
-// K = d_h + d_R as above (one 16-token half); the value product uses the 16x16x16
-// fp16 MFMA, whose B operand (16 tokens x 16 rows) is the lane's own four softmax
-// weights in the D layout of the score tile, and whose A operand (16 features x 16
-// tokens) is one transposing LDS read.  The kernel stays HBM-bound: the half-rate
-// value MFMA has ample slack.  Grid, split-K and outputs as gqa_decode_kernel.
-// ---------------------------------------------------------------------------
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// softmax_tile for one 16-token half: sc[i] is token 4q + i.  Returns P as the B operand
+// of the 16x16x16 fp16 MFMA (16 tokens x 16 rows).
 
 __device__ __forceinline__ f16x4 softmax_tile4(SoftmaxState& st, float (&sc)[4], bool& rescale, float& alpha) {
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -335,31 +326,59 @@ __device__ __forceinline__ f16x4 softmax_tile4(SoftmaxState& st, float (&sc)[4],
     return __builtin_bit_cast(f16x4, u32x2{pack2h(p[0], p[1]), pack2h(p[2], p[3])});
 }
 
-template <int G, int NW, int RPW>
-__global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
+// ---------------------------------------------------------------------------
+// Tiles fed by direct loads: gqa_dma_kernel<G, NW, RPW, TR>, TR = 16 or 32 cache rows
+// per tile.  Tiles go from global memory straight into one of two LDS buffers
+// (global_load_lds_dwordx4) and are used there as loaded, in bf16: no staging registers,
+// no conversion pass through LDS and one barrier per tile.  At step k, after the barrier
+// that published tile k (buffer k % 2), every wave issues its share of tile k + 1's loads
+// into buffer (k + 1) % 2, whose last reader was step k - 1, computes tile k, and waits
+// for its own loads.  So a tile's loads are in flight for a whole step, where the
+// register-staged kernel above issues them only after the previous tile's LDS store.
+// The scores run on the bf16 MFMA against the queries as given; the value operands are
+// converted to fp16 in registers after the transposing read, so that P keeps fp16's 11
+// bits.  At TR = 16 the value product is the 16x16x16 fp16 MFMA, whose B operand (16
+// tokens x 16 rows) is the lane's own four softmax weights in the D layout of the score
+// tile; at TR = 32 it is the 16x16x32 one, as in gqa_decode_kernel.  Two buffers of 32
+// rows fit LDS up to g = 4; at g = 8 the tiles have 16 rows (2 x 68.6 KB).
+// A buffer holds TR rows at a stride of W + 16 elements (8 x odd dwords modulo the 64
+// banks), rounded up to whole 64-lane instructions of 16-byte slots; the two pad slots of
+// a row and any spare slots load the row's (or the tile's) first 16 bytes, a line loaded
+// anyway, and are never read.  Rows past the chunk load the tile's first row (finite data,
+// masked, P = 0).  Grid, work split and outputs as gqa_decode_kernel.
+// ---------------------------------------------------------------------------
+template <int G, int NW, int RPW, int TR>
+__global__ __launch_bounds__(NW * 64) void gqa_dma_kernel(
     const u16* __restrict__ q_nope, const u16* __restrict__ q_rope,
     const u16* __restrict__ cache, int64_t bstride, const int32_t* __restrict__ ctx_lens,
     int max_ctx, int h_q, int s_q, int chunk, int n_split, int nz, int cap, int batch, float scale_log2,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
-    constexpr int T16 = 16;
+    static_assert(TR == 16 || TR == 32, "16- or 32-row tiles");
+    static_assert(kChunkAlign % TR == 0, "chunks are whole tiles");
     constexpr int W = 2 * G * DH + DR;
     constexpr int STRIDE = W + 16;
-    constexpr int NT = NW * 64;
-    constexpr int NLOAD = (T16 * (W / 8) + NT - 1) / NT;
-    __shared__ __attribute__((aligned(16))) u16 lds[T16 * STRIDE];
+    constexpr int SROW = STRIDE / 8;                       // 16-byte slots per LDS row
+    constexpr int CPR = W / 8;                             // data slots per row
+    constexpr int NINST = (TR * SROW + 63) / 64;           // 64-lane load instructions per tile
+    constexpr int BSLOTS = NINST * 64;                     // slots per buffer (with the spare ones)
+    constexpr int MI = (NINST + NW - 1) / NW;              // load instructions per wave (at most)
+    constexpr int NH = TR / 16;                            // 16-token halves per tile
+    static_assert((STRIDE / 2) % 64 % 16 == 8, "row stride is 8 x odd dwords modulo 64 banks");
+    __shared__ __attribute__((aligned(16))) u16 lds[2 * BSLOTS * 8];
 
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int zb = slot % nz;
     const int unit = (slot / nz) * 8 + xcd;
     if (unit >= n_split * batch) return;
     int b, p, t0, t1;
-    if (!chunk_of_item<NT>(unit, ctx_lens, batch, max_ctx, chunk, cap, reinterpret_cast<int*>(lds), b, p, t0, t1)) return;
+    if (!chunk_of_item<NW * 64>(unit, ctx_lens, batch, max_ctx, chunk, cap, reinterpret_cast<int*>(lds), b, p, t0, t1))
+        return;
     const int L = clampi(ctx_lens[b], 0, max_ctx);
-    __syncthreads();
-    const int ntiles = (t1 - t0 + T16 - 1) / T16;
+    __syncthreads();                          // the item is known to every thread before the tiles reuse LDS
+    const int ntiles = (t1 - t0 + TR - 1) / TR;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q4 = lane >> 4, r16 = lane & 15;
     const int hpg = h_q / G;
     const int rows_g = s_q * hpg;
@@ -380,12 +399,36 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
         qrow[rg] = (b * s_q + s) * h_q + h;
     }
 
-    // the first tile's loads go out before the queries', so the two round trips to memory
-    // overlap at the start of every item
+    // Byte offset within a tile of the 16 bytes that slot (wave + NW m) * 64 + lane of a
+    // buffer carries; instruction wave + NW m exists for m < MI - 1 and, for the first
+    // NINST % NW waves (or all when it divides), for m = MI - 1.
     const u16* seq = cache + (size_t)b * bstride;
-    u32x4 reg[NLOAD];
-    load_tile<W, NT, NLOAD, T16>(reg, seq + (size_t)t0 * W, min(T16, t1 - t0), tid);
-    f16x8 qv[RPW][6];
+    uint32_t off[MI];
+#pragma unroll
+    for (int m = 0; m < MI; ++m) {
+        const int sl = (wave + NW * m) * 64 + lane;
+        const int r = sl / SROW, c = sl - (sl / SROW) * SROW;
+        off[m] = (sl < TR * SROW) ? (uint32_t)((r * W + (c < CPR ? c : 0) * 8) * 2) : 0u;
+    }
+    const bool last_inst = (wave + NW * (MI - 1)) < NINST;
+    const uint32_t lbase = lds_addr(lds);
+    auto dma_tile = [&](int it) {
+        const u16* tsrc = seq + (size_t)(t0 + it * TR) * W;
+        const uint32_t tbuf = lbase + (uint32_t)((it & 1) * BSLOTS * 16);
+        const int rows = t1 - t0 - it * TR;
+        const uint32_t lim = rows >= TR ? 0xffffffffu : (uint32_t)(rows * W * 2);
+#pragma unroll
+        for (int m = 0; m < MI; ++m) {
+            if (m < MI - 1 || last_inst) {
+                const uint32_t o = off[m] < lim ? off[m] : off[m] % (uint32_t)(W * 2);
+                dma16_nt(tsrc, o, tbuf + (uint32_t)((wave + NW * m) * 1024));
+            }
+        }
+    };
+    dma_tile(0);
+
+    // queries as the B operand of S^T = K Q^T: k-steps 0..3 over q^N, 4..5 over q^R
+    bf16x8 qv[RPW][6];
 #pragma unroll
     for (int rg = 0; rg < RPW; ++rg)
 #pragma unroll
@@ -393,9 +436,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
             if (row_ok[rg]) {
                 const u16* src = kk < 4 ? q_nope + (size_t)qrow[rg] * DH + kk * 32 + q4 * 8
                                         : q_rope + (size_t)qrow[rg] * DR + (kk - 4) * 32 + q4 * 8;
-                qv[rg][kk] = as_f16x8(bf8_to_h8(*reinterpret_cast<const u32x4*>(src)));
+                qv[rg][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src));
             } else {
-                qv[rg][kk] = zero_f16x8();
+                qv[rg][kk] = zero_bf16x8();
             }
         }
 
@@ -409,38 +452,46 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
     for (int rg = 0; rg < RPW; ++rg) st[rg] = SoftmaxState{kNegInf, 0.f};
 
     for (int it = 0; it < ntiles; ++it) {
-        const int tb = t0 + it * T16;
-        if (it > 0) __syncthreads();
-        store_tile<W, STRIDE, NT, NLOAD, T16>(lds, reg, tid);
-        __syncthreads();
-        if (it + 1 < ntiles) {
-            const int tn = tb + T16;
-            load_tile<W, NT, NLOAD, T16>(reg, seq + (size_t)tn * W, min(T16, t1 - tn), tid);
-        }
+        // this wave's loads of tile it have landed (nothing else of it is in flight), and
+        // after the barrier everyone's have, and tile it - 1's buffer is free
+        wait_vmcnt<0>();
+        block_sync();
+        if (it + 1 < ntiles) dma_tile(it + 1);
         if (!active) continue;
+        const int tb = t0 + it * TR;
+        const u16* tile = lds + (it & 1) * BSLOTS * 8;
 
-        f16x4 pb[RPW];
+        f16x4 pb4[RPW];
+        f16x8 pb8[RPW];
         {
-            floatx4 acc[RPW][2] = {};
+            // two independent accumulator chains per 16-token half and row tile
+            floatx4 acc[RPW][NH][2] = {};
 #pragma unroll
             for (int kk = 0; kk < 6; ++kk) {
                 const int col = kk < 4 ? j * DH + kk * 32 + q4 * 8 : 2 * G * DH + (kk - 4) * 32 + q4 * 8;
-                const f16x8 a = ld_f16x8(lds + r16 * STRIDE + col);
 #pragma unroll
-                for (int rg = 0; rg < RPW; ++rg) acc[rg][kk & 1] = mfma16h(a, qv[rg][kk], acc[rg][kk & 1]);
+                for (int th = 0; th < NH; ++th) {
+                    const bf16x8 a = ld_bf16x8(tile + (th * 16 + r16) * STRIDE + col);
+#pragma unroll
+                    for (int rg = 0; rg < RPW; ++rg)
+                        acc[rg][th][kk & 1] = mfma16(a, qv[rg][kk], acc[rg][th][kk & 1]);
+                }
             }
 #pragma unroll
             for (int rg = 0; rg < RPW; ++rg) {
-                float sc[4];
+                float sc[4 * NH];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = tb + q4 * 4 + i;
-                    const float v = acc[rg][0][i] + acc[rg][1][i];
-                    sc[i] = (row_ok[rg] && t < t1 && t < nvis[rg]) ? v * scale_log2 : kNegInf;
-                }
+                for (int th = 0; th < NH; ++th)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = tb + th * 16 + q4 * 4 + i;
+                        const float v = acc[rg][th][0][i] + acc[rg][th][1][i];
+                        sc[th * 4 + i] = (row_ok[rg] && t < t1 && t < nvis[rg]) ? v * scale_log2 : kNegInf;
+                    }
                 bool rescale;
                 float alpha;
-                pb[rg] = softmax_tile4(st[rg], sc, rescale, alpha);
+                if constexpr (TR == 16) pb4[rg] = softmax_tile4(st[rg], sc, rescale, alpha);
+                else pb8[rg] = softmax_tile(st[rg], sc, rescale, alpha);
                 if (__builtin_expect(rescale, 0)) {
                     asm volatile("" ::: "memory");
 #pragma unroll
@@ -448,14 +499,23 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
                 }
             }
         }
-        // A operand: feature vcol + 16n + r16 at the lane's tokens 4q4 .. 4q4 + 3
-        const u16* vbase = lds + (4 * q4 + (r16 >> 2)) * STRIDE + (G + j) * DH + 4 * (r16 & 3);
+        // A operand: feature (G + j) d_h + 16n + r16 at the lane's slot tokens, read
+        // transposed in bf16 and converted to fp16
+        const u16* vbase = tile + (4 * q4 + (r16 >> 2)) * STRIDE + (G + j) * DH + 4 * (r16 & 3);
 #pragma unroll
         for (int n = 0; n < DH / 16; ++n) {
-            const f16x4 a = __builtin_bit_cast(f16x4, lds_read_tr16(vbase + 16 * n));
+            const u32x2 lo = lds_read_tr16(vbase + 16 * n);
+            if constexpr (TR == 16) {
+                const f16x4 a = __builtin_bit_cast(f16x4, u32x2{bf2_to_h2(lo[0]), bf2_to_h2(lo[1])});
 #pragma unroll
-            for (int rg = 0; rg < RPW; ++rg)
-                oacc[rg][n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb[rg], oacc[rg][n], 0, 0, 0);
+                for (int rg = 0; rg < RPW; ++rg)
+                    oacc[rg][n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pb4[rg], oacc[rg][n], 0, 0, 0);
+            } else {
+                const u32x2 hi = lds_read_tr16(vbase + 16 * n + 16 * STRIDE);
+                const f16x8 a = as_f16x8(u32x4{bf2_to_h2(lo[0]), bf2_to_h2(lo[1]), bf2_to_h2(hi[0]), bf2_to_h2(hi[1])});
+#pragma unroll
+                for (int rg = 0; rg < RPW; ++rg) oacc[rg][n] = mfma16h(a, pb8[rg], oacc[rg][n]);
+            }
         }
     }
 
@@ -472,19 +532,19 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode16_kernel(
     }
 }
 
-template <int G, int NW, int RPW>
-hipError_t launch_gqa16_t(const DecodeArgs& a, hipStream_t st) {
+template <int G, int NW, int RPW, int TR>
+hipError_t launch_gqa_dma_t(const DecodeArgs& a, hipStream_t st) {
     const int rows_g = a.s_q * (a.h_q / a.g);
     const int waves = G * ((rows_g + 15) / 16) / RPW;
     const int nz = (waves + NW - 1) / NW;
     const int units = a.n_split * a.batch;
     // work items that run at once
-    static const int per_cu = blocks_per_cu(gqa_decode16_kernel<G, NW, RPW>, NW * 64);
+    static const int per_cu = blocks_per_cu(gqa_dma_kernel<G, NW, RPW, TR>, NW * 64);
     const int cap = per_cu * a.cus / nz;
     dim3 grid(((units + 7) / 8) * 8 * nz);
     hipError_t e = record_if(a.ev_before, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gqa_decode16_kernel<G, NW, RPW>), grid, dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((gqa_dma_kernel<G, NW, RPW, TR>), grid, dim3(NW * 64), 0, st,
                        (const u16*)a.q_nope, (const u16*)a.q_rope, (const u16*)a.cache, a.bstride,
                        a.ctx_lens, a.max_ctx, a.h_q, a.s_q, a.chunk, a.n_split, nz, cap, a.batch, a.scale * kLog2e,
                        a.part_o, a.part_lse);
@@ -516,17 +576,29 @@ hipError_t launch_gqa_t(const DecodeArgs& a, hipStream_t st) {
 
 // 8 waves per block (with 1024-thread blocks the 128-register cap spills the staging
 // registers).  Two row tiles per wave when a group has an even number of them and one
-// tile per wave would take more than one block; at g = 8 that runs on 16-token tiles,
-// since the 32-row 2112-wide tile's staging registers plus two row tiles' state exceed
-// 256 (47 spills).
+// tile per wave would take more than one block.  Which kernel, as measured on MI355X
+// (kernel time, HBM fraction of 8 TB/s):
+//   - two row tiles per wave: direct loads (g = 8, s_q = 2, ragged 1K-32K: 0.777 ->
+//     0.816 against register-staged 16-row tiles; g = 4, s_q = 2: 0.695 -> 0.731), but
+//     at g = 1 (640-byte rows: a 32-row tile is 20 KB, too little in flight per block);
+//   - one row tile per wave at g = 2 and 4: direct loads (g = 2: 0.62-0.66 -> 0.69-0.76;
+//     g = 4: within 3 % either way at 4096-token chunks, 0.75 -> 0.77 at 1024);
+//   - one row tile per wave at g = 8: register-staged 32-row tiles (0.860 against 0.852
+//     at 4096-token chunks) except for chunks of at most 1024 tokens (0.800 -> 0.822);
+//   - g = 1: register-staged, two 32-row tiles ahead.
 template <int G>
 hipError_t launch_gqa_g(const DecodeArgs& a, hipStream_t st) {
     const int rt = (a.s_q * (a.h_q / a.g) + 15) / 16;
-    if (rt % 2 == 0 && G * rt > 8) {
-        if constexpr (G <= 4) return launch_gqa_t<G, 8, 2, 1>(a, st);
-        else return launch_gqa16_t<G, 8, 2>(a, st);
+    const bool two = rt % 2 == 0 && G * rt > 8;
+    if constexpr (G == 1) {
+        return two ? launch_gqa_t<1, 8, 2, 1>(a, st) : launch_gqa_t<1, 8, 1, 2>(a, st);
+    } else if constexpr (G == 8) {
+        if (two) return launch_gqa_dma_t<8, 8, 2, 16>(a, st);
+        if (a.chunk <= 1024) return launch_gqa_dma_t<8, 8, 1, 16>(a, st);
+        return launch_gqa_t<8, 8, 1, 1>(a, st);
+    } else {
+        return two ? launch_gqa_dma_t<G, 8, 2, 32>(a, st) : launch_gqa_dma_t<G, 8, 1, 32>(a, st);
     }
-    return launch_gqa_t<G, 8, 1, (G <= 4 ? 2 : 1)>(a, st);
 }
 
 }  // namespace
