@@ -32,8 +32,9 @@
  *   - q_rope and the k_R columns of the cache hold keys/queries with the
  *     rotary embedding already applied.
  *   - Operand range (bf16 storage): some products run on fp16 copies of the bf16
- *     inputs: the GQA and sparse decodes' queries and expanded rows (k_R included),
- *     and the latent rows c_t in the absorb decode's weighted sum u.  Values whose
+ *     inputs: the value columns V_j of the GQA and sparse decodes, their queries and
+ *     key columns (k_R included) too in the kernels that some shapes select, and the
+ *     latent rows c_t in the absorb decode's weighted sum u.  Values whose
  *     magnitude lies in fp16's normal range [2^-14, 65504] are converted exactly;
  *     smaller magnitudes keep fp16's subnormal spacing 2^-24 (an absolute error of at
  *     most 2^-24 per element); magnitudes above 65504 are outside the supported range
