@@ -40,7 +40,7 @@ KERNEL_SOURCES = {
     "gqa_sparse": ["latent_kv_cache_amd/csrc/decode_sparse.hip", "latent_kv_cache_amd/csrc/common.h"],
 }
 KERNEL_PREFIXES = {
-    "gqa_decode": ("gqa_decode_kernel", "gqa_decode16_kernel"),
+    "gqa_decode": ("gqa_decode_kernel", "gqa_dma_kernel"),
     "absorb_decode": ("absorb_decode_kernel",),
     "gqa_sparse": ("gqa_sparse_kernel",),
 }
