@@ -115,7 +115,6 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
     const int b = bs / s_q, s = bs - (bs / s_q) * s_q;
     const int h = j * hpg + hh;
     const size_t qrow = ((size_t)b * s_q + s) * h_q + h;
-    unsigned char* dst = qrec + qrow * QREC;
 
     // k-slot e of lane group q4 in k-step kd is d = 32kd + 4q4 + e (e < 4) or
     // 32kd + 16 + 4q4 + (e - 4): the transposing reads of the four lane groups then lie
@@ -148,12 +147,15 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
         acc[mt] = a;
     }
 
-    if (!ok) return;
-    // x = q~ * scale * log2(e) (fp32) as hi = bf16(x) and lo = bf16(x - hi)
+    // x = q~ * scale * log2(e) (fp32) as hi = bf16(x) and lo = bf16(x - hi), staged in
+    // LDS (over the W_UK tile, once every wave is done with it) as [row][hi 128 | lo 128]
+    // so that the records leave in whole 256-byte segments: written straight from the
+    // MFMA layout, every store instruction would touch 16 rows with 32 bytes each.
+    constexpr int OSTR = 2 * PRO_COLS + 8;   // staged row stride (u16): 132 dwords
+    static_assert(64 * OSTR <= DH * PRO_STRIDE, "the staged records fit over the W_UK tile");
+    __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < PRO_COLS / 16; ++mt) {
-        // columns 128 qc + 16 mt + 4 q4 + i of the natural latent order
-        const int col = qc * PRO_COLS + 16 * mt + 4 * q4;
         u16 hs[4], ls[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -161,17 +163,45 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
             hs[i] = f2bf(x);
             ls[i] = f2bf(x - bf2f(hs[i]));
         }
-        *reinterpret_cast<u32x2*>(dst + QHI + col * 2) = u32x2{pack2(hs[0], hs[1]), pack2(hs[2], hs[3])};
-        *reinterpret_cast<u32x2*>(dst + QLO + col * 2) = u32x2{pack2(ls[0], ls[1]), pack2(ls[2], ls[3])};
+        u16* srow = wt + (wave * 16 + r16) * OSTR + 16 * mt + 4 * q4;
+        *reinterpret_cast<u32x2*>(srow) = u32x2{pack2(hs[0], hs[1]), pack2(hs[2], hs[3])};
+        *reinterpret_cast<u32x2*>(srow + PRO_COLS) = u32x2{pack2(ls[0], ls[1]), pack2(ls[2], ls[3])};
     }
-    // q^R: 64 elements, copied by the first quarter's block; lane group q4 copies
-    // elements 16 q4 .. 16 q4 + 15
+    __syncthreads();
+    // query row of block row r, and whether it exists
+    auto row_of = [&](int r, bool& valid) -> size_t {
+        const int it = blockIdx.x * 64 + r;
+        valid = it < nrows;
+        const int bs_ = valid ? it / hpg : 0;
+        const int hh_ = valid ? it - bs_ * hpg : 0;
+        const int b_ = bs_ / s_q, s_ = bs_ - (bs_ / s_q) * s_q;
+        return ((size_t)b_ * s_q + s_) * h_q + j * hpg + hh_;
+    };
+    // 64 rows x 32 pieces of 16 bytes (16 of hi, 16 of lo): 8 per thread; a wave
+    // instruction writes two rows' hi and lo segments
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int pc = k * 256 + tid;
+        const int r = pc >> 5, c = pc & 31;
+        bool valid;
+        unsigned char* rec = qrec + row_of(r, valid) * QREC;
+        if (valid) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(wt + r * OSTR + c * 8);
+            const int off = c < 16 ? QHI + (qc * PRO_COLS + c * 8) * 2 : QLO + (qc * PRO_COLS + (c - 16) * 8) * 2;
+            *reinterpret_cast<u32x4*>(rec + off) = v;
+        }
+    }
+    // q^R: 64 elements (128 bytes, 8 pieces) per row, copied by the first quarter's block
     if (qc == 0) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int off = q4 * 16 + c * 8;
-            *reinterpret_cast<u32x4*>(dst + QROPE + off * 2) =
-                *reinterpret_cast<const u32x4*>(q_rope + qrow * DR + off);
+        for (int k = 0; k < 2; ++k) {
+            const int pc = k * 256 + tid;
+            const int r = pc >> 3, c = pc & 7;
+            bool valid;
+            const size_t qr = row_of(r, valid);
+            if (valid)
+                *reinterpret_cast<u32x4*>(qrec + qr * QREC + QROPE + c * 16) =
+                    *reinterpret_cast<const u32x4*>(q_rope + qr * DR + c * 8);
         }
     }
 }
