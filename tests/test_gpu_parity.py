@@ -130,12 +130,14 @@ def test_multi_token_shapes(gqla, g, s_q):
     both_paths(cfg, lens, gqla, 0, what=f"cfg4 g{g} s_q{s_q}")
 
 
-@pytest.mark.parametrize("h_q,g,s_q", [(128, 1, 2), (128, 2, 2), (128, 4, 2), (128, 8, 2), (32, 8, 1), (128, 8, 1)])
+@pytest.mark.parametrize("h_q,g,s_q", [(128, 1, 2), (128, 2, 2), (128, 4, 2), (128, 8, 2), (32, 8, 1), (128, 8, 1),
+                                       (128, 8, 4), (64, 4, 3), (128, 2, 1)])
 def test_gqa_direct_load_tiles(gqla, h_q, g, s_q):
     """The GQA kernels that load tiles straight into LDS (two 32-row buffers at g = 2 and
     4, two 16-row ones at g = 8; g = 1 stays on register-staged tiles): one and two row
-    tiles per wave, lengths that end one row into a tile, on a tile boundary and
-    mid-tile, over three chunks of at most 1024 tokens."""
+    tiles per wave, several workgroups per item (g = 8, s_q = 4), lengths that end one
+    row into a tile, on a tile boundary and mid-tile, over three chunks of at most 1024
+    tokens."""
     cfg = synth.config(3, g=g, s_q=s_q).with_(batch=5, h_q=h_q)
     w = gu.workload(cfg, lens=[1000, 77, 33, 17, s_q], max_ctx=1000)
     note(f"direct-load gqa h_q={h_q} g={g} s_q={s_q} lens={list(w.lens)}")
