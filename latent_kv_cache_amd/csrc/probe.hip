@@ -13,8 +13,12 @@ namespace gqla {
 
 namespace {
 
-constexpr int kReadThreads = 512;
-constexpr int kReadUnroll = 8;       // 16-byte loads in flight per lane
+// Four 256-thread blocks per CU with four 16-byte loads in flight per lane read fastest
+// of the shapes tried on MI355X (7.01 TB/s over 4 GiB; two 512-thread blocks with eight
+// loads 6.86, 16 or more blocks per CU 6.0-6.5).
+constexpr int kReadThreads = 256;
+constexpr int kReadUnroll = 4;       // 16-byte loads in flight per lane
+constexpr int kReadBlocksPerCu = 4;
 
 // Streams [base, base + n16 * 16) once, with nontemporal loads (the policy of the
 // streaming decode kernel).  Block k reads its own contiguous span (the
@@ -73,7 +77,8 @@ hipError_t probe_read_bandwidth(const void* buf, size_t bytes, int cus, hipStrea
     for (int rep = 0; rep < 4 && e == hipSuccess; ++rep) {   // the first pass warms up
         e = hipEventRecord(e0, st);
         if (e != hipSuccess) break;
-        hipLaunchKernelGGL(read_probe_kernel, dim3(2 * cus), dim3(kReadThreads), 0, st, (const u32x4*)buf, n16,
+        hipLaunchKernelGGL(read_probe_kernel, dim3(kReadBlocksPerCu * cus), dim3(kReadThreads), 0, st,
+                           (const u32x4*)buf, n16,
                            (uint32_t*)buf, -1);
         e = hipGetLastError();
         if (e == hipSuccess) e = hipEventRecord(e1, st);
