@@ -1,4 +1,4 @@
-// bf16 MFMA GQA decode kernel for gfx950.
+// bf16 MFMA GQA decode kernels for gfx950.
 //
 // Method: "GQLA: Group-Query Latent Attention for Hardware-Adaptive LLM
 // Decoding", technical summary section 2 (Architecture, GQA path).  Per sequence b,
@@ -8,17 +8,19 @@
 // over one context chunk per workgroup (split-K).  Each workgroup writes the chunk's
 // normalised output and its log-sum-exp; launch_combine merges them.
 //
-// Tiling.  A workgroup streams its chunk in tiles of 32 cache rows.  A tile is
-// one contiguous span of HBM (rows of a sequence are packed), loaded with
-// 16-byte vector loads into registers one tile ahead and stored into LDS with
-// a 32-byte pad per row.  On gfx950 a row stride of 8 x (odd) dwords modulo the 64
-// LDS banks lets the 16-byte operand reads of 16 rows, and the transposing reads of
-// 4 rows x 32 bytes, proceed at close to the full LDS rate (a 16-byte pad, 36 dwords
-// mod 64, measured at about 60 % of it).
-// HBM holds bf16; the tile is converted to fp16 on its way into LDS (exact for
-// bf16 values within fp16's range) and the contractions run on fp16 MFMA, so the
-// softmax weights P, which the kernel itself rounds, keep 10 mantissa bits instead
-// of 7.
+// Tiling.  A workgroup streams its chunk in tiles of cache rows.  A tile is one
+// contiguous span of HBM (rows of a sequence are packed), held in LDS with a 32-byte
+// pad per row.  On gfx950 a row stride of 8 x (odd) dwords modulo the 64 LDS banks lets
+// the 16-byte operand reads of 16 rows, and the transposing reads of 4 rows x 32 bytes,
+// proceed at close to the full LDS rate (a 16-byte pad, 36 dwords mod 64, measured at
+// about 60 % of it).  Two ways to fill it:
+//   - gqa_decode_kernel: 16-byte vector loads into registers one (or two) 32-row tiles
+//     ahead, converted from bf16 to fp16 on the way into LDS (exact for bf16 values
+//     within fp16's range); both contractions run on fp16 MFMA;
+//   - gqa_dma_kernel (below): loads straight into one of two LDS buffers, used there in
+//     bf16: scores on the bf16 MFMA, value operands converted to fp16 in registers.
+// Either way the softmax weights P, which the kernel itself rounds, are fp16 and keep
+// 10 mantissa bits instead of bf16's 7.
 // Each wave owns 16 query rows (the N = 16 side of the 16x16x32 MFMA: the 16 heads
 // of a group at h_q/g = 16) and keeps its queries and accumulators in registers:
 //   S^T[token][row] = K_tile . Q^T   (A = cache rows from LDS, B = queries)
