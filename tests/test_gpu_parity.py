@@ -334,10 +334,6 @@ def test_full_size_long_context_sampled(gqla):
     both_paths(cfg, None, gqla, 0, seqs=[0, 15], what="full cfg5", end_to_end=True)
 
 
-if __name__ == "__main__":  # pragma: no cover
-    sys.exit(pytest.main([__file__, "-v"]))
-
-
 @pytest.mark.parametrize("h_q,g,s_q", [(16, 8, 2), (64, 8, 1), (32, 4, 2), (32, 1, 1)])
 def test_absorb_column_split_rows(gqla, h_q, g, s_q):
     """32 and 64 query rows per sequence (s_q * h_q), the workgroups whose eight waves
@@ -366,3 +362,7 @@ def test_binding_rejects_mismatched_tensors(gqla):
         gqla.decode_absorb(sh, w.q_nope, w.q_rope, w.w_uk[:4], w.w_uv, w.latent, w.ctx_lens, out)
     torch.cuda.synchronize()
     assert bool(torch.all(out == 0))
+
+
+if __name__ == "__main__":  # pragma: no cover
+    sys.exit(pytest.main([__file__, "-v"]))
