@@ -14,10 +14,12 @@
 // bf16 kernel.  One wave per work item (sequence, query token, group, 16-row tile of
 // the group's heads, list chunk); the four waves of a block are independent, each with
 // its own LDS slice, so the kernel has no block barrier.  Per tile of 32 listed rows:
-//   - the scores read their K_j and k_R operands straight from global memory (each
-//     lane's 16 bytes are 8 consecutive elements of one gathered row, the MFMA A
-//     layout) and run on the bf16 MFMA against the bf16 queries: all products exact;
-//   - the 32 V_j rows are gathered into the wave's LDS slice (rows outside the list or
+//   - the 32 K_j rows are gathered four rows of 256 bytes per instruction, written to
+//     the wave's LDS slice and read back in the score MFMA's A layout; the k_R operands
+//     come straight from global memory in that layout (each lane's 16 bytes are 8
+//     consecutive elements of one gathered row); the scores run on the bf16 MFMA against
+//     the bf16 queries: all products exact;
+//   - the 32 V_j rows are then gathered into the same slice (rows outside the list or
 //     the sequence as zeros) and read back transposed as the A operand of
 //     O^T += V^T P^T;
 //   - P is split into two bf16 terms (hi + lo, about 16 significant bits) so that the
@@ -121,18 +123,31 @@ __global__ __launch_bounds__(NWS * 64) void gqa_sparse_kernel(
         const int t0 = il[r16], t1 = il[16 + r16];
         const u16* row0 = seq + (size_t)((t0 >= 0 && t0 < L) ? t0 : 0) * W;
         const u16* row1 = seq + (size_t)((t1 >= 0 && t1 < L) ? t1 : 0) * W;
+        constexpr int NV = TT * (DH / 8) / 64;
+        // K_j rows of the tile: lane piece c = k * 64 + lane is row c / 16, 8 columns
+        // (c % 16) * 8, so that an instruction gathers 4 rows x 256 bytes.  Loaded in the
+        // score MFMA's own layout (16 rows x 64 bytes per instruction), random rows gather
+        // at about 0.8 of that rate on MI355X; the rows reach that layout through the wave's
+        // LDS slice instead.  Nontemporal, as V_j below.  k_R (two k-steps) keeps the MFMA
+        // layout and the default policy: the other groups' lists read it too, mostly from L2.
+        u32x4 kv[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int c = k * 64 + lane;
+            const int t = il[c >> 4];
+            kv[k] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(seq + (size_t)((t >= 0 && t < L) ? t : 0) * W + j * DH + (c & 15) * 8));
+        }
         bf16x8 ka[6], kc[6];
 #pragma unroll
-        for (int kk = 0; kk < 6; ++kk) {
-            const int col = kk < 4 ? j * DH + kk * 32 + q4 * 8 : 2 * g * DH + (kk - 4) * 32 + q4 * 8;
+        for (int kk = 4; kk < 6; ++kk) {
+            const int col = 2 * g * DH + (kk - 4) * 32 + q4 * 8;
             ka[kk] = ld_bf16x8(row0 + col);
             kc[kk] = ld_bf16x8(row1 + col);
         }
-        // V_j rows of the tile: chunk c = 16 per row.  Nontemporal: a V_j row belongs to one
-        // group and is not read again this step (on MI355X 234 -> 217 us at 2048 rows per
-        // (b, j)); K_j and k_R keep the default policy, k_R because the other groups' lists
-        // re-read it through L2.
-        constexpr int NV = TT * (DH / 8) / 64;
+        // V_j rows of the tile: chunk c = 16 per row.  Nontemporal: a V_j (or K_j) row
+        // belongs to one group and is not read again this step (on MI355X 234 -> 217 us at
+        // 2048 rows per (b, j) for V_j; with K_j too, and K_j through LDS, 212 -> 194 us).
         u32x4 vv[NV];
         bool vok[NV];
 #pragma unroll
@@ -143,13 +158,25 @@ __global__ __launch_bounds__(NWS * 64) void gqa_sparse_kernel(
             vv[k] = __builtin_nontemporal_load(
                 reinterpret_cast<const u32x4*>(seq + (size_t)(vok[k] ? t : 0) * W + (g + j) * DH + (c & 15) * 8));
         }
+        // K_j into the slice and back in the MFMA layout (rows 0..15, then 16..31)
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int c = k * 64 + lane;
+            *reinterpret_cast<u32x4*>(vl + (c >> 4) * VSTRIDE + (c & 15) * 8) = kv[k];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            ka[kk] = ld_bf16x8(vl + r16 * VSTRIDE + kk * 32 + q4 * 8);
+            kc[kk] = ld_bf16x8(vl + (16 + r16) * VSTRIDE + kk * 32 + q4 * 8);
+        }
         floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
         for (int kk = 0; kk < 6; ++kk) {
             acc0 = mfma16(ka[kk], qv[kk], acc0);
             acc1 = mfma16(kc[kk], qv[kk], acc1);
         }
-        // into the wave's LDS slice, rows outside the list or the sequence as zeros
+        // V_j into the same slice (after the K_j reads above: one wave's LDS operations
+        // complete in order), rows outside the list or the sequence as zeros
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int c = k * 64 + lane;
