@@ -23,11 +23,17 @@ constexpr int RK = 512;   // latent width
 constexpr int W = RK + DR;
 constexpr int TT = 32;    // tokens per tile
 
-// Absorbed-query record of one query row, written by the prologue and read once by the
-// attention kernel (QREC bytes, 16-byte aligned):
-//   [0, 1024)     hi: bf16 of x = q~ * scale * log2(e), latent column order
-//   [1024, 2048)  lo: bf16 of x - hi (the rounding residual of hi, rounded again)
-//   [2048, 2176)  q^R (bf16, as given), unscaled
+// Absorbed-query records, written by the prologue and read once by the attention
+// kernel, QREC bytes per query row.  Per row they hold
+//   hi: bf16 of x = q~ * scale * log2(e) (512 elements),
+//   lo: bf16 of x - hi (the rounding residual of hi, rounded again) (512),
+//   q^R (bf16, as given, unscaled) (64),
+// stored for each 16 consecutive query rows (b * s_q * h_q + rho, rho = 16 m .. 16 m + 15)
+// as one block of 34 pieces of 1 KB, in the order the score wave of those rows loads them:
+// piece kk (hi, kk = 0..15), 16 + kk (lo) or 32 + kr (q^R, kr = 0..1) holds, at byte
+// 16 (16 q + r) (lane (q, r) of the wave), elements 32 kk + 8 q .. + 7 of row r.  Each
+// load instruction then reads 1 KB of contiguous memory; the rows themselves, 16 rows x
+// 64 bytes per instruction, load at well under that rate.  (rec_piece gives the offset.)
 // hi + lo carries x to about 16 significant bits, against the bf16 latent rows as they
 // are stored (every product exact in the fp32 accumulation).  A single 8- or 11-bit
 // rounding of q~ gives score errors that grow with |score|: with sharp softmaxes (peak
@@ -35,7 +41,13 @@ constexpr int TT = 32;    // tokens per tile
 // fold; the hi + lo pair leaves them far below it, at one extra MFMA per latent k-step.
 // bf16 keeps fp32's exponent range, so no operand of the score product needs scaling.
 constexpr int QREC = 2176;
-constexpr int QHI = 0, QLO = 1024, QROPE = 2048;
+constexpr int QHI = 0, QLO = 16, QROPE = 32;   // first piece of each part
+
+// Byte offset of piece m of query row `row`'s 16-row block, lane (q, r) position for r =
+// row % 16 (the caller adds nothing else).
+__device__ __forceinline__ size_t rec_piece(size_t row, int m, int q) {
+    return (row / 16) * (16 * (size_t)QREC) + (size_t)m * 1024 + (size_t)(q * 16 + (int)(row % 16)) * 16;
+}
 
 // ---------------------------------------------------------------------------
 // Prologue: one block per (64 rows of group j, j, quarter qc of the latent columns); 4
@@ -184,11 +196,12 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
         const int pc = k * 256 + tid;
         const int r = pc >> 5, c = pc & 31;
         bool valid;
-        unsigned char* rec = qrec + row_of(r, valid) * QREC;
+        const size_t row = row_of(r, valid);
         if (valid) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(wt + r * OSTR + c * 8);
-            const int off = c < 16 ? QHI + (qc * PRO_COLS + c * 8) * 2 : QLO + (qc * PRO_COLS + (c - 16) * 8) * 2;
-            *reinterpret_cast<u32x4*>(rec + off) = v;
+            // staged piece c: columns 8 (c % 16) of the quarter, k-step 4 qc + (c % 16) / 4
+            const int kk = 4 * qc + (c & 15) / 4, q = c & 3;
+            *reinterpret_cast<u32x4*>(qrec + rec_piece(row, (c < 16 ? QHI : QLO) + kk, q)) = v;
         }
     }
     // q^R: 64 elements (128 bytes, 8 pieces) per row, copied by the first quarter's block
@@ -200,7 +213,7 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
             bool valid;
             const size_t qr = row_of(r, valid);
             if (valid)
-                *reinterpret_cast<u32x4*>(qrec + qr * QREC + QROPE + c * 16) =
+                *reinterpret_cast<u32x4*>(qrec + rec_piece(qr, QROPE + c / 4, c & 3)) =
                     *reinterpret_cast<const u32x4*>(q_rope + qr * DR + c * 8);
         }
     }
@@ -391,15 +404,15 @@ __global__ __launch_bounds__((NS + NV) * 64) void absorb_decode_kernel(
         SoftmaxState st{kNegInf, 0.f};
         if (active) {
             const int rho = z * R + 16 * sw + r16;
-            const unsigned char* rec = qrec + ((size_t)b * RQ + rho) * QREC;
+            // this row tile's block of records (16 rows; RQ is a multiple of 16)
+            const unsigned char* blk = qrec + ((size_t)b * RQ + z * R + 16 * sw) / 16 * (16 * (size_t)QREC) + lane * 16;
 #pragma unroll
             for (int kk = 0; kk < RK / 32; ++kk) {
-                qhi[kk] = ld_bf16x8(reinterpret_cast<const u16*>(rec + QHI) + kk * 32 + q4 * 8);
-                qlo[kk] = ld_bf16x8(reinterpret_cast<const u16*>(rec + QLO) + kk * 32 + q4 * 8);
+                qhi[kk] = ld_bf16x8(reinterpret_cast<const u16*>(blk + (QHI + kk) * 1024));
+                qlo[kk] = ld_bf16x8(reinterpret_cast<const u16*>(blk + (QLO + kk) * 1024));
             }
 #pragma unroll
-            for (int kr = 0; kr < DR / 32; ++kr)
-                qro[kr] = ld_bf16x8(reinterpret_cast<const u16*>(rec + QROPE) + kr * 32 + q4 * 8);
+            for (int kr = 0; kr < DR / 32; ++kr) qro[kr] = ld_bf16x8(reinterpret_cast<const u16*>(blk + (QROPE + kr) * 1024));
             nvis = clampi(L - s_q + rho / h_q + 1, 0, L);
         }
         auto sstep = [&](int k) {
