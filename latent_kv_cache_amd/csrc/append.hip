@@ -19,17 +19,11 @@
 // an fp32 angle would be off by far more than the storage precision.
 #include "common.h"
 #include "launch.h"
+#include "append_rope.h"
 
 namespace gqla {
 
 namespace {
-
-__device__ __forceinline__ double to_f64(u16 v) { return (double)bf2f(v); }
-__device__ __forceinline__ double to_f64(float v) { return (double)v; }
-__device__ __forceinline__ void store_from_f64(u16* p, double x) { *p = f2bf((float)x); }
-__device__ __forceinline__ void store_from_f64(float* p, double x) { *p = (float)x; }
-
-constexpr int kMaxHalf = 128;   // d_R <= 256
 
 // grid = batch * s_q blocks (one per new token), 256 threads
 template <typename T>
@@ -37,50 +31,8 @@ __global__ __launch_bounds__(256) void append_rope_kernel(
     const T* __restrict__ c_new, const T* __restrict__ kr_new, const T* __restrict__ q_raw, T* __restrict__ q_out,
     const int32_t* __restrict__ ctx_lens, int max_ctx, int s_q, int h_q, int r_kv, int d_r, double theta,
     T* __restrict__ latent, int64_t lbs, T* __restrict__ group, int64_t gbs, int gw) {
-#pragma clang fp contract(off)
-    __shared__ double cs[kMaxHalf], sn[kMaxHalf];
-    const int b = blockIdx.x / s_q, s = blockIdx.x - (blockIdx.x / s_q) * s_q;
-    const int L = clampi(ctx_lens[b], 0, max_ctx);
-    const int t = L - s_q + s;
-    if (t < 0) return;   // the sequence is shorter than its new tokens: no row for this one
-    const int half = d_r / 2;
-    const int tid = threadIdx.x;
-    for (int k = tid; k < half; k += 256) {
-        const double f = pow(theta, (-2.0 * (double)k) / (double)d_r);
-        const double a = (double)t * f;
-        cs[k] = cos(a);
-        sn[k] = sin(a);
-    }
-    __syncthreads();
-
-    const size_t tok = (size_t)b * s_q + s;
-    T* row = latent + (size_t)b * lbs + (size_t)t * (r_kv + d_r);
-    const T* cn = c_new + tok * r_kv;
-    for (int e = tid; e < r_kv; e += 256) row[e] = cn[e];
-
-    const T* kr = kr_new + tok * d_r;
-    T* grow = group ? group + (size_t)b * gbs + (size_t)t * (gw + d_r) + gw : nullptr;
-    for (int k = tid; k < half; k += 256) {
-        const double x = to_f64(kr[k]), y = to_f64(kr[k + half]);
-        const double r0 = x * cs[k] - y * sn[k];
-        const double r1 = x * sn[k] + y * cs[k];
-        store_from_f64(row + r_kv + k, r0);
-        store_from_f64(row + r_kv + k + half, r1);
-        if (grow) {
-            store_from_f64(grow + k, r0);
-            store_from_f64(grow + k + half, r1);
-        }
-    }
-    if (q_raw) {
-        const T* qs = q_raw + tok * h_q * d_r;
-        T* qd = q_out + tok * h_q * d_r;
-        for (int i = tid; i < h_q * half; i += 256) {
-            const int h = i / half, k = i - (i / half) * half;
-            const double x = to_f64(qs[h * d_r + k]), y = to_f64(qs[h * d_r + k + half]);
-            store_from_f64(qd + h * d_r + k, x * cs[k] - y * sn[k]);
-            store_from_f64(qd + h * d_r + k + half, x * sn[k] + y * cs[k]);
-        }
-    }
+    append_rope_token<T, 256>(blockIdx.x, c_new, kr_new, q_raw, q_out, ctx_lens, max_ctx, s_q, h_q, r_kv, d_r, theta,
+                              latent, lbs, group, gbs, gw);
 }
 
 // fp32 expansion of the new rows: grid = batch * s_q blocks, thread per output column
@@ -108,6 +60,8 @@ hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t st) {
     const int tokens = a.batch * a.s_q;
     if (tokens == 0) return hipSuccess;
     const int gw = 2 * a.g * a.d_h;
+    // bf16 with the group cache: one launch for the rotations and the expansion
+    if (bf16 && a.group_cache) return launch_append_fused_bf16(a, st);
     if (bf16) {
         hipLaunchKernelGGL(append_rope_kernel<u16>, dim3(tokens), dim3(256), 0, st, (const u16*)a.c_new,
                            (const u16*)a.kr_new, (const u16*)a.q_rope_raw, (u16*)a.q_rope_out, a.ctx_lens, a.max_ctx,
@@ -121,7 +75,6 @@ hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.group_cache) return e;
-    if (bf16) return launch_append_expand_bf16(a, st);
     hipLaunchKernelGGL(append_expand_f32_kernel, dim3(tokens), dim3(256), 0, st, (const float*)a.c_new,
                        (const float*)a.w_uk, (const float*)a.w_uv, a.ctx_lens, a.max_ctx, a.s_q, a.g, a.r_kv, a.d_h,
                        (float*)a.group_cache, a.group_bstride, a.d_r);

@@ -17,6 +17,7 @@
 // and leave as 16-byte stores that write whole 512-byte row segments.
 #include "common.h"
 #include "launch.h"
+#include "append_rope.h"
 
 namespace gqla {
 
@@ -222,21 +223,22 @@ __global__ __launch_bounds__(NW * 64) void expand_kernel(
 // Expansion of the decode step's new rows (the append): row r < batch * s_q of c_new
 // ([batch][s_q][r_kv], packed) is token s = r % s_q of sequence b = r / s_q, which sits
 // at t = L_b - s_q + s of the group cache (rows with t < 0 are skipped).  Same tiling
-// as expand_kernel with one 64-row tile per block; the rotary key columns are written
-// by the append's rotation kernel.
-template <int G>
-__global__ __launch_bounds__(512) void append_expand_kernel(
-    const u16* __restrict__ c_new, const u16* __restrict__ w_uk, const u16* __restrict__ w_uv,
+// as expand_kernel with one 64-row tile per block of NT threads (bx: NT / 4 output
+// columns, 16 per wave; by: 64 rows); the rotary key columns are written by the
+// append's rotation.
+template <int G, int NT>
+__device__ __forceinline__ void append_expand_block(
+    int bx, int by, const u16* __restrict__ c_new, const u16* __restrict__ w_uk, const u16* __restrict__ w_uv,
     const int32_t* __restrict__ ctx_lens, int max_ctx, int s_q, int rows, u16* __restrict__ gc, int64_t gbs) {
     constexpr int WOUT = 2 * G * DH + DR;
     __shared__ __attribute__((aligned(16))) u16 lds[XT * XSTRIDE];
 
-    const int r0 = blockIdx.y * XT;
+    const int r0 = by * XT;
     const int nr = min(XT, rows - r0);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int q4 = lane >> 4, r16 = lane & 15;
-    const int col0 = blockIdx.x * 128 + wave * 16;
+    const int col0 = bx * (NT / 4) + wave * 16;
     const int colA = col0 + r16;
     const u16* wrow = colA < G * DH ? w_uk + (size_t)colA * RK : w_uv + (size_t)(colA - G * DH) * RK;
 
@@ -244,17 +246,17 @@ __global__ __launch_bounds__(512) void append_expand_kernel(
 #pragma unroll
     for (int ks = 0; ks < RK / 32; ++ks) wa[ks] = ld_bf16x8(wrow + ks * 32 + q4 * 8);
     {
-        u32x4 v[XT * (RK / 8) / 512];
+        u32x4 v[XT * (RK / 8) / NT];
 #pragma unroll
-        for (int k = 0; k < XT * (RK / 8) / 512; ++k) {
-            const int c = k * 512 + tid;
+        for (int k = 0; k < XT * (RK / 8) / NT; ++k) {
+            const int c = k * NT + tid;
             const int r = c >> 6, col = c & 63;
             v[k] = u32x4{0u, 0u, 0u, 0u};
             if (r < nr) v[k] = *reinterpret_cast<const u32x4*>(c_new + (size_t)(r0 + r) * RK + col * 8);
         }
 #pragma unroll
-        for (int k = 0; k < XT * (RK / 8) / 512; ++k) {
-            const int c = k * 512 + tid;
+        for (int k = 0; k < XT * (RK / 8) / NT; ++k) {
+            const int c = k * NT + tid;
             *reinterpret_cast<u32x4*>(lds + (c >> 6) * XSTRIDE + (c & 63) * 8) = v[k];
         }
     }
@@ -280,12 +282,35 @@ __global__ __launch_bounds__(512) void append_expand_kernel(
     }
 }
 
+// The whole bf16 append in one launch: blocks below nexp expand the new rows (block i:
+// columns bx = i % (2 g d_h / 64), rows by = i / that), the rest rotate one new token
+// each.  The two parts touch disjoint outputs and read only inputs, so they run side by
+// side instead of one launch after the other.  256 threads: at 512 the expansion's
+// weights, operands and accumulators do not fit the registers of two waves per SIMD.
+constexpr int APT = 256;
 template <int G>
-hipError_t launch_append_expand_g(const AppendArgs& a, hipStream_t st) {
+__global__ __launch_bounds__(APT) void append_fused_kernel(
+    const u16* __restrict__ c_new, const u16* __restrict__ kr_new, const u16* __restrict__ q_raw,
+    u16* __restrict__ q_out, const int32_t* __restrict__ ctx_lens, int max_ctx, int s_q, int h_q, int rows,
+    double theta, u16* __restrict__ latent, int64_t lbs, const u16* __restrict__ w_uk, const u16* __restrict__ w_uv,
+    u16* __restrict__ gc, int64_t gbs, int nexp) {
+    constexpr int NCB = 2 * G * DH / (APT / 4);
+    const int i = blockIdx.x;
+    if (i < nexp)
+        append_expand_block<G, APT>(i % NCB, i / NCB, c_new, w_uk, w_uv, ctx_lens, max_ctx, s_q, rows, gc, gbs);
+    else
+        append_rope_token<u16, APT>(i - nexp, c_new, kr_new, q_raw, q_out, ctx_lens, max_ctx, s_q, h_q, RK, DR, theta,
+                                    latent, lbs, gc, gbs, 2 * G * DH);
+}
+
+template <int G>
+hipError_t launch_append_fused_g(const AppendArgs& a, hipStream_t st) {
     const int rows = a.batch * a.s_q;
-    dim3 grid(2 * G * DH / 128, (rows + XT - 1) / XT);
-    hipLaunchKernelGGL(append_expand_kernel<G>, grid, dim3(512), 0, st, (const u16*)a.c_new, (const u16*)a.w_uk,
-                       (const u16*)a.w_uv, a.ctx_lens, a.max_ctx, a.s_q, rows, (u16*)a.group_cache, a.group_bstride);
+    const int nexp = (2 * G * DH / (APT / 4)) * ((rows + XT - 1) / XT);
+    hipLaunchKernelGGL(append_fused_kernel<G>, dim3(nexp + rows), dim3(APT), 0, st, (const u16*)a.c_new,
+                       (const u16*)a.kr_new, (const u16*)a.q_rope_raw, (u16*)a.q_rope_out, a.ctx_lens, a.max_ctx,
+                       a.s_q, a.h_q, rows, (double)a.theta, (u16*)a.latent, a.latent_bstride, (const u16*)a.w_uk,
+                       (const u16*)a.w_uv, (u16*)a.group_cache, a.group_bstride, nexp);
     return hipGetLastError();
 }
 
@@ -304,12 +329,13 @@ hipError_t launch_expand_g(const ExpandArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_append_expand_bf16(const AppendArgs& a, hipStream_t st) {
+hipError_t launch_append_fused_bf16(const AppendArgs& a, hipStream_t st) {
+    if (a.batch * a.s_q == 0) return hipSuccess;
     switch (a.g) {
-        case 1: return launch_append_expand_g<1>(a, st);
-        case 2: return launch_append_expand_g<2>(a, st);
-        case 4: return launch_append_expand_g<4>(a, st);
-        case 8: return launch_append_expand_g<8>(a, st);
+        case 1: return launch_append_fused_g<1>(a, st);
+        case 2: return launch_append_fused_g<2>(a, st);
+        case 4: return launch_append_fused_g<4>(a, st);
+        case 8: return launch_append_fused_g<8>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

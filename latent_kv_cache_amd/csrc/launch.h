@@ -73,7 +73,7 @@ struct AppendArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t st);
-hipError_t launch_append_expand_bf16(const AppendArgs& a, hipStream_t st);
+hipError_t launch_append_fused_bf16(const AppendArgs& a, hipStream_t st);   // rotations and expansion, one launch
 
 // bf16 MFMA path (r_kv = 512, d_r = 64, d_h = 128)
 hipError_t launch_absorb_bf16(const DecodeArgs& a, hipStream_t st);
