@@ -189,32 +189,35 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(
         const int b_ = bs_ / s_q, s_ = bs_ - (bs_ / s_q) * s_q;
         return ((size_t)b_ * s_q + s_) * h_q + j * hpg + hh_;
     };
-    // 64 rows x 32 pieces of 16 bytes (16 of hi, 16 of lo): 8 per thread; a wave
-    // instruction writes two rows' hi and lo segments
+    // 64 rows x 32 pieces of 16 bytes (16 of hi, 16 of lo), in units of one piece m of
+    // 16 consecutive block rows: unit u = 4 k + wave is rows 16 (u / 8) + r, piece
+    // (u % 8 < 4 ? hi : lo) k-step 4 qc + u % 4, lane (q, r).  Where those rows are 16
+    // consecutive query rows (h_q / g >= 16), a wave instruction writes one whole 1 KB
+    // piece of their record block.
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const int pc = k * 256 + tid;
-        const int r = pc >> 5, c = pc & 31;
+        const int u = k * 4 + wave;
+        const int r = 16 * (u >> 3) + r16, mi = u & 7;
         bool valid;
         const size_t row = row_of(r, valid);
         if (valid) {
+            const int c = (mi < 4 ? 0 : 16) + 4 * (mi & 3) + q4;   // staged piece: 8 columns
             const u32x4 v = *reinterpret_cast<const u32x4*>(wt + r * OSTR + c * 8);
-            // staged piece c: columns 8 (c % 16) of the quarter, k-step 4 qc + (c % 16) / 4
-            const int kk = 4 * qc + (c & 15) / 4, q = c & 3;
-            *reinterpret_cast<u32x4*>(qrec + rec_piece(row, (c < 16 ? QHI : QLO) + kk, q)) = v;
+            *reinterpret_cast<u32x4*>(qrec + rec_piece(row, (mi < 4 ? QHI : QLO) + 4 * qc + (mi & 3), q4)) = v;
         }
     }
-    // q^R: 64 elements (128 bytes, 8 pieces) per row, copied by the first quarter's block
+    // q^R: 64 elements (8 pieces of 16 bytes) per row, copied by the first quarter's block,
+    // in the same units (u = 4 k + wave: rows 16 (u / 2) + r, piece kr = u % 2)
     if (qc == 0) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int pc = k * 256 + tid;
-            const int r = pc >> 3, c = pc & 7;
+            const int u = k * 4 + wave;
+            const int r = 16 * (u >> 1) + r16, kr = u & 1;
             bool valid;
             const size_t qr = row_of(r, valid);
             if (valid)
-                *reinterpret_cast<u32x4*>(qrec + rec_piece(qr, QROPE + c / 4, c & 3)) =
-                    *reinterpret_cast<const u32x4*>(q_rope + qr * DR + c * 8);
+                *reinterpret_cast<u32x4*>(qrec + rec_piece(qr, QROPE + kr, q4)) =
+                    *reinterpret_cast<const u32x4*>(q_rope + qr * DR + kr * 32 + q4 * 8);
         }
     }
 }
