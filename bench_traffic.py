@@ -3,13 +3,13 @@
 Two counter passes of bench.py (one counter each; a pass holds at most the
 counters one hardware pass can collect):
 
-  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic_FETCH_SIZE -o pmc -- \
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d out/traffic_FETCH_SIZE -o pmc -- \
       python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
-  rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic_WRITE_SIZE -o pmc -- \
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d out/traffic_WRITE_SIZE -o pmc -- \
       python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
   python bench_traffic.py \
-      gpurun_out/traffic_FETCH_SIZE/pmc_counter_collection.csv \
-      gpurun_out/traffic_WRITE_SIZE/pmc_counter_collection.csv BENCH_LINE_JSON [--write]
+      out/traffic_FETCH_SIZE/pmc_counter_collection.csv \
+      out/traffic_WRITE_SIZE/pmc_counter_collection.csv BENCH_LINE_JSON [--write]
 
 FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  bench.py runs one plain device
 copy of 1 GiB before timing; its readings give the scale of each counter (bytes
